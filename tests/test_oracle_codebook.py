@@ -1,0 +1,295 @@
+"""Pins of the codebook oracle against facts fixed outside the oracle.
+
+Each test checks the oracle against something other than itself: values
+printed on the pages (QLC Tables 1 and 2), closed forms, brute force on tiny
+alphabets, textbook inequalities and a published worked example of canonical
+code assignment.
+"""
+import itertools
+import math
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import codebook as cb
+
+
+# --------------------------------------------------------------------------
+# histogram / pooling
+# --------------------------------------------------------------------------
+
+def test_histogram_brute_force():
+    rng = random.Random(1)
+    data = [rng.randrange(256) for _ in range(3000)] + [7] * 50
+    counts = cb.histogram(np.array(data, dtype=np.uint8))
+    for s in range(256):
+        assert counts[s] == sum(1 for v in data if v == s)
+    assert sum(counts) == len(data)
+
+
+def test_pooled_counts_is_sum_of_batches():
+    rng = np.random.default_rng(3)
+    batches = [rng.integers(0, 256, 1000, dtype=np.uint8) for _ in range(4)]
+    pooled = cb.pooled_counts(batches)
+    allbytes = np.concatenate(batches)
+    assert pooled == cb.histogram(allbytes)
+
+
+def test_floor_keeps_every_symbol_codable():
+    counts = [0] * 256
+    counts[3] = 1000
+    counts[200] = 5
+    w = cb.floor_weights(counts)
+    assert min(w) == 1 and w[3] == 1000 and w[200] == 5
+    lengths = cb.package_merge(w)
+    assert all(1 <= l <= 12 for l in lengths)
+    assert cb.kraft(lengths) == 1
+
+
+# --------------------------------------------------------------------------
+# package-merge: optimality and closed forms
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(12))
+def test_package_merge_matches_brute_force(seed):
+    rng = random.Random(seed)
+    n = rng.randint(2, 8)
+    # skewed weights so that short limits bind
+    weights = [rng.choice([1, 1, 2, 3, 5, 8, 13, 40, 200, 1000]) for _ in range(n)]
+    min_l = max(1, math.ceil(math.log2(n)))
+    for L in range(min_l, n):
+        if n == 8 and L > 4:
+            break  # keep the exhaustive search small
+        lengths = cb.package_merge(weights, L)
+        assert max(lengths) <= L
+        assert cb.kraft(lengths) <= 1
+        assert cb.cost(weights, lengths) == cb.brute_force_cost(weights, L), (weights, L)
+
+
+def test_brute_force_itself_on_hand_case():
+    # weights 1,1,2,4: Huffman lengths 3,3,2,1 cost 1*3+1*3+2*2+4*1 = 14;
+    # with L = 2 every length is 2: cost 16.
+    assert cb.brute_force_cost([1, 1, 2, 4], 3) == 14
+    assert cb.brute_force_cost([1, 1, 2, 4], 2) == 16
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_kraft_exactly_one_and_limit(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 257))
+    w = [int(v) for v in rng.integers(1, 10**6, n)]
+    if seed % 3 == 0:
+        w = [int(2 ** (v % 40)) for v in range(n)]  # heavy skew: limit binds
+    lengths = cb.package_merge(w, 12)
+    assert max(lengths) <= 12
+    assert cb.kraft(lengths) == Fraction(1)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_equals_huffman_cost_when_huffman_fits(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(2, 200))
+    w = [int(v) for v in rng.integers(1, 1000, n)]
+    h = cb.huffman_lengths(w)
+    if max(h) <= 12:
+        assert cb.cost(w, cb.package_merge(w, 12)) == cb.cost(w, h)
+    # L = n - 1 never binds: package-merge is then plain Huffman
+    if n <= 64:
+        assert cb.cost(w, cb.package_merge(w, max(n - 1, 1))) == cb.cost(w, h)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_huffman_within_entropy_plus_one(seed):
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(2, 257))
+    w = [int(v) for v in rng.integers(1, 10**5, n)]
+    h = cb.huffman_lengths(w)
+    tot = sum(w)
+    avg = cb.cost(w, h) / tot
+    H = cb.entropy_bits(w)
+    assert H - 1e-12 <= avg < H + 1
+    # the length limit costs at most what it must: never below Huffman
+    assert cb.cost(w, cb.package_merge(w, 12)) >= cb.cost(w, h)
+
+
+def test_uniform_gives_all_eights():
+    assert cb.package_merge([7] * 256, 12) == [8] * 256
+
+
+def test_dyadic_gives_minus_log2_p():
+    # p_s = 2^-k_s with a complete dyadic distribution, max k = 12
+    ks = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 12]
+    assert sum(Fraction(1, 2 ** k) for k in ks) == 1
+    w = [2 ** (12 - k) for k in ks]
+    lengths = cb.package_merge(w, 12)
+    assert lengths == ks
+    # average length equals the entropy exactly
+    tot = sum(w)
+    assert abs(cb.cost(w, lengths) / tot - cb.entropy_bits(w)) < 1e-12
+
+
+def test_fibonacci_limit_binds():
+    fib = [1, 1]
+    while len(fib) < 20:
+        fib.append(fib[-1] + fib[-2])
+    h = cb.huffman_lengths(fib)
+    assert max(h) == 19  # unconstrained depth n-1
+    pm = cb.package_merge(fib, 12)
+    assert max(pm) == 12
+    assert cb.kraft(pm) == 1
+    assert cb.cost(fib, pm) > cb.cost(fib, h)
+
+
+def test_tie_rule_is_deterministic_and_weight_monotone():
+    # Equal weights and a skewed tail: heavier symbols never get longer codes,
+    # and among equal weights a lower byte value never gets a longer code
+    # (leaves are ordered by (weight, byte value); the merge keeps leaves first).
+    rng = np.random.default_rng(7)
+    w = [int(v) for v in rng.integers(1, 6, 256)]
+    lengths = cb.package_merge(w, 12)
+    for a in range(256):
+        for b in range(256):
+            if w[a] > w[b]:
+                assert lengths[a] <= lengths[b]
+            if w[a] == w[b] and a < b:
+                assert lengths[a] >= lengths[b]
+
+
+# --------------------------------------------------------------------------
+# canonical codes
+# --------------------------------------------------------------------------
+
+def test_canonical_matches_deflate_worked_example(golden):
+    rows = golden("deflate_canonical_example.txt")
+    lengths = [int(r[1]) for r in rows]
+    codes = cb.canonical_codes(lengths)
+    for (s, l, want), c in zip(rows, codes):
+        assert cb.code_string(c, int(l)) == want
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_canonical_prefix_free_and_ordered(seed):
+    rng = np.random.default_rng(300 + seed)
+    counts = [int(v) for v in rng.integers(0, 10**4, 256)]
+    lengths, codes = cb.huffman_codebook(counts)
+    strs = [cb.code_string(c, l) for c, l in zip(codes, lengths)]
+    assert len(set(strs)) == 256
+    for i in range(256):
+        for j in range(256):
+            if i != j:
+                assert not strs[j].startswith(strs[i])
+    order = sorted(range(256), key=lambda s: (lengths[s], s))
+    assert codes[order[0]] == 0
+    assert codes[order[-1]] == (1 << lengths[order[-1]]) - 1  # Kraft = 1
+    for a, b in zip(order, order[1:]):
+        # read as binary fractions, codes strictly increase along the order
+        assert Fraction(codes[a] + 1, 1 << lengths[a]) <= Fraction(codes[b], 1 << lengths[b])
+
+
+# --------------------------------------------------------------------------
+# Quad Length Codes: the printed tables
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("table", ["qlc_table1.txt", "qlc_table2.txt"])
+def test_qlc_layout_reproduces_printed_table(golden, table):
+    rows = golden(table)
+    bits = [int(r[3]) for r in rows] + [7, 7]  # areas 7-8 unprinted: any value
+    layout = cb.qlc_layout(bits)
+    for r, (a, slots, b, length, start) in zip(rows, layout):
+        area, code, nsym, sbits, clen, lo, hi = r
+        assert int(area) == a + 1
+        assert code == format(a, "03b")
+        assert int(nsym) == slots == 2 ** int(sbits)
+        assert int(clen) == length == 3 + int(sbits)
+        assert (int(lo), int(hi)) == (start, start + slots - 1)
+
+
+def test_qlc_table_lengths_are_the_printed_ones(golden):
+    assert [int(r[4]) for r in golden("qlc_table1.txt")] == [6, 6, 6, 6, 6, 7]
+    assert [int(r[4]) for r in golden("qlc_table2.txt")] == [4, 6, 6, 6, 6, 8]
+
+
+def test_qlc_codes_follow_table2_ranks(golden):
+    rows = golden("qlc_table2.txt")
+    bits = (1, 3, 3, 3, 3, 5, 6, 7)
+    rng = np.random.default_rng(11)
+    counts = [int(v) for v in rng.integers(0, 10**6, 256)]
+    lengths, codes, rank_of, order = cb.qlc_code(counts, bits)
+    # rank r = position in descending-count order, ties by byte value
+    for r in range(255):
+        a, b = order[r], order[r + 1]
+        assert counts[a] > counts[b] or (counts[a] == counts[b] and a < b)
+    for area, code, nsym, sbits, clen, lo, hi in rows:
+        for r in range(int(lo), int(hi) + 1):
+            s = order[r]
+            assert lengths[s] == int(clen)
+            want = code + format(r - int(lo), "0%sb" % sbits)
+            assert cb.code_string(codes[s], lengths[s]) == want
+
+
+def test_qlc_gelu_layout_closed_forms():
+    bits = (1, 3, 3, 3, 3, 5, 6, 7)
+    counts = list(range(256, 0, -1))  # rank r is byte r
+    lengths, codes, rank_of, order = cb.qlc_code(counts, bits)
+    assert order == list(range(256))
+    assert all(lengths[r] == 9 for r in range(66, 130))
+    assert all(lengths[r] == 10 for r in range(130, 256))
+    assert cb.kraft(lengths) == Fraction(511, 512)
+    # exactly 8 of the 4096 12-bit prefixes start with no codeword
+    strs = [cb.code_string(c, l) for c, l in zip(codes, lengths)]
+    covered = sum(2 ** (12 - len(s)) for s in strs)
+    assert 4096 - covered == 8
+    # prefix-free
+    for i in range(256):
+        for j in range(256):
+            if i != j:
+                assert not strs[j].startswith(strs[i])
+
+
+def test_qlc_equals_canonical_when_lengths_do_not_decrease():
+    # Lengths grow across areas here, so the QLC codes are the canonical codes
+    # of (length, rank) order: a cross-check of the two code-assignment rules.
+    bits = (1, 3, 3, 3, 3, 5, 6, 7)
+    rng = np.random.default_rng(5)
+    counts = [int(v) for v in rng.integers(0, 1000, 256)]
+    lengths, codes, rank_of, order = cb.qlc_code(counts, bits)
+    by_rank_len = [lengths[order[r]] for r in range(256)]
+    canon = cb.canonical_codes(by_rank_len)
+    for r in range(256):
+        assert codes[order[r]] == canon[r]
+
+
+def test_qlc_rejects_short_cover():
+    with pytest.raises(ValueError):
+        cb.qlc_code([1] * 256, (1, 1, 1, 1, 1, 1, 1, 1))
+
+
+# --------------------------------------------------------------------------
+# measurement quantities
+# --------------------------------------------------------------------------
+
+def test_entropy_closed_forms():
+    assert cb.entropy_bits([5] * 256) == pytest.approx(8.0, abs=1e-12)
+    assert cb.entropy_bits([0] * 255 + [9]) == 0.0
+    assert cb.entropy_bits([1, 1]) == pytest.approx(1.0)
+    assert cb.entropy_bits([2, 1, 1]) == pytest.approx(1.5)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_gibbs_fixed_code_costs_at_least_entropy(seed):
+    rng = np.random.default_rng(400 + seed)
+    prev = [int(v) for v in rng.integers(0, 10**4, 256)]
+    cur = [int(v) for v in rng.integers(0, 10**4, 256)]
+    lengths, _ = cb.huffman_codebook(prev)
+    n = sum(cur)
+    b = cb.coded_bits(cur, lengths) / n
+    assert b >= cb.entropy_bits(cur) - 1e-12
+    shard = cb.per_shard_lengths(cur)
+    assert cb.coded_bits(cur, shard) <= cb.coded_bits(cur, lengths)
+
+
+def test_compressibility_reading():
+    assert cb.compressibility(8.0) == 0.0
+    assert cb.compressibility(6.728) == pytest.approx(0.159)
