@@ -1,0 +1,375 @@
+#!/usr/bin/env python3
+"""Throughput of fixed-codebook encode + decode on one MI355X.
+
+One step = the whole hot path over one batch: pc_encode (codeword lookup,
+bit-length scan, cross-chunk scan, bit packing, stores) followed by pc_decode
+(side-index sub-streams through the 12-bit peek table) of the same stream.
+Inputs are resident in HBM before timing starts; the codebook is built
+offline from previous batches and is not timed.
+
+Prints one JSON line.  `value` = uncompressed bytes per second of the round
+trip (n / step time), in GB/s.  Also reported: encode-only and decode-only
+GB/s from HIP events on the launch stream, bits/symbol against the entropy,
+the HBM roofline of the slower kernel, and the CPU oracle timed on a bounded
+sample of the same stream (with its outputs compared to the GPU's).
+
+    python bench.py [--steps K] [--warmup W] [--workload stream_1g]
+    python bench.py --pmc-summary FETCH_DIR WRITE_DIR   # write profiles/traffic.txt
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+KERNEL_SOURCES = {
+    "encode": os.path.join(ROOT, "static_codebook_lossless_amd", "csrc", "encode.hip"),
+    "decode": os.path.join(ROOT, "static_codebook_lossless_amd", "csrc", "decode.hip"),
+}
+KERNEL_NAMES = {"encode": "encode_kernel", "decode": "decode_kernel"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kind: str) -> str:
+    with open(KERNEL_SOURCES[kind], "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 counters (FETCH_SIZE / WRITE_SIZE, KiB per
+# dispatch), scaled by what the same counters read for a plain copy of
+# known size that runs in the same program.
+# ---------------------------------------------------------------------------
+
+def _read_counter_csv(d, counter):
+    import csv
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError("no counter_collection.csv under " + d)
+    rows = []
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id")))
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir, copy_bytes, out=TRAFFIC_FILE):
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _read_counter_csv(d, counter)
+        per = {}
+        for name, val, _ in rows:
+            per.setdefault(name, []).append(val * 1024.0)  # KiB -> bytes
+        copy_vals = [v for k, vs in per.items() if "copy" in k.lower() or "elementwise" in k.lower() for v in vs]
+        if not copy_vals:
+            raise RuntimeError("no copy kernel found for the %s scale" % counter)
+        scale = copy_bytes / (sum(copy_vals) / len(copy_vals))
+        res[counter] = {"scale": scale, "kernels": {k: sum(v) / len(v) for k, v in per.items()}}
+    lines = ["# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of bench.py.",
+             "# Each counter is scaled by copy_bytes / counter(plain copy of copy_bytes bytes).",
+             "copy_bytes %d" % copy_bytes,
+             "fetch_scale %.6f" % res["FETCH_SIZE"]["scale"],
+             "write_scale %.6f" % res["WRITE_SIZE"]["scale"]]
+    for kind, kname in KERNEL_NAMES.items():
+        f = [v for k, v in res["FETCH_SIZE"]["kernels"].items() if kname in k]
+        w = [v for k, v in res["WRITE_SIZE"]["kernels"].items() if kname in k]
+        if f and w:
+            fb = f[0] * res["FETCH_SIZE"]["scale"]
+            wb = w[0] * res["WRITE_SIZE"]["scale"]
+            lines.append("kernel %s sha %s fetch_bytes %.0f write_bytes %.0f" % (kind, source_sha(kind), fb, wb))
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_traffic(kind):
+    """Scaled HBM bytes per dispatch of `kind`, or None when absent/stale."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        p = line.split()
+        if len(p) >= 8 and p[0] == "kernel" and p[1] == kind:
+            if p[3] != source_sha(kind):
+                return None
+            return float(p[5]) + float(p[7])
+    return None
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same stream.
+# ---------------------------------------------------------------------------
+
+def cpu_baseline_leg(x_np, counts_prev, kind, qlc_bits, chunk, gpu_streams, target_seconds, threads):
+    """Time the oracle's bit-serial encoder and decoder on the first chunks
+    of the stream and compare their outputs with the GPU's for those chunks."""
+    import numpy as np
+
+    from oracle import codebook as ocb
+    from oracle import coder
+
+    book = ocb.codebook([int(c) for c in counts_prev], kind, qlc_bits)
+    nchunks_total = (x_np.size + chunk - 1) // chunk
+
+    def run(nch):
+        part = x_np[: min(nch * chunk, x_np.size)]
+        t0 = time.perf_counter()
+        s = coder.encode(part, book["lengths"], book["codes"], chunk, threads=threads)
+        t1 = time.perf_counter()
+        y, rc = coder.decode(s, part.size, chunk, book, threads=threads)
+        t2 = time.perf_counter()
+        return part, s, y, rc, t1 - t0, t2 - t1
+
+    pilot = min(nchunks_total, max(threads, 8))
+    part, s, y, rc, te, td = run(pilot)
+    rate = part.size / max(te + td, 1e-6)
+    want = int(min(nchunks_total, max(pilot, (target_seconds * rate) // chunk)))
+    if want > pilot:
+        part, s, y, rc, te, td = run(want)
+    nch = (part.size + chunk - 1) // chunk
+    cwo = gpu_streams["chunk_word_offset"][: nch + 1]
+    words = int(cwo[nch])
+    spc = chunk // 256
+    nsub = s["sub_off"].size
+    parity = {
+        "chunks": int(nch),
+        "payload_words_equal": bool(np.array_equal(gpu_streams["payload"](words), s["payload"])),
+        "chunk_bits_equal": bool(np.array_equal(gpu_streams["chunk_bits"][:nch], s["chunk_bits"])),
+        "chunk_word_offset_equal": bool(np.array_equal(cwo, s["chunk_word_offset"])),
+        "sub_off_equal": bool(np.array_equal(gpu_streams["sub_off"][:nsub], s["sub_off"])),
+        "oracle_round_trip": bool(rc == 0 and np.array_equal(y, part)),
+    }
+    del spc
+    return {
+        "value": round(part.size / (te + td) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "first %d of %d chunks (%d bytes) of the same stream; bit-serial C encode %.2f s + "
+                  "decode %.2f s" % (nch, nchunks_total, part.size, te, td),
+        "encode_GBps": round(part.size / te / 1e9, 4),
+        "decode_GBps": round(part.size / td / 1e9, 4),
+        "cpu_model": _cpu_model(),
+    }, parity
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------------------
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="stream_1g")
+    ap.add_argument("--decoder", default="lut12", choices=["lut12", "qlc"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.pmc_summary:
+        import workloads as W
+
+        cb = args.copy_bytes or W.WORKLOADS[args.workload].n * 2
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], cb)
+        return 0
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this coder needs no second device and no figure at "
+              "several GPUs is measured (asked for --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import static_codebook_lossless_amd as pc
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]
+    n, chunk = w.n, w.chunk
+
+    # ---- inputs (host synthesis, then resident in HBM) -----------------
+    log("generating %s (%d bytes) and %d previous batch(es)" % (w.name, n, len(w.prev_seeds)))
+    t0 = time.perf_counter()
+    counts_dev = torch.zeros(256, dtype=torch.int64, device=dev)
+    for s in w.prev_seeds:
+        prev = torch.from_numpy(W.make(w.name, s)).to(dev)
+        pc.pc_histogram(prev, counts_dev)  # pooled counts of previous batches
+        del prev
+    counts_prev = counts_dev.cpu().numpy().astype(np.uint64)
+    x_np = W.make(w.name, 0)
+    x = torch.from_numpy(x_np).to(dev)
+    torch.cuda.synchronize()
+    log("inputs ready in %.1f s" % (time.perf_counter() - t0))
+
+    blob = pc.pc_codebook_build(counts_prev, w.kind, w.qlc_bits)
+    dcb = blob.to(dev)
+    fields = pc.codebook_fields(blob)
+    outs = pc.alloc_encode_outputs(n, chunk, dev)
+    dec_out = torch.empty(n, dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    decode = pc.pc_decode_qlc if args.decoder == "qlc" else pc.pc_decode
+
+    # plain device copy of the input: context for the roofline
+    cpy = torch.empty_like(x)
+    for _ in range(3):
+        cpy.copy_(x)
+    torch.cuda.synchronize()
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record()
+    for _ in range(5):
+        cpy.copy_(x)
+    ce1.record()
+    torch.cuda.synchronize()
+    copy_GBps = 2 * n * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
+    del cpy
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        enc = pc.pc_encode(dcb, x, chunk, outs)
+        if evs:
+            evs[1].record()
+        decode(dcb, enc, out=dec_out, status=status)
+        if evs:
+            evs[2].record()
+        return enc
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        enc = step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        enc = step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- checks and stream statistics ---------------------------------
+    st = int(status.item())
+    same = bool(torch.equal(dec_out, x))
+    if st != 0 or not same:
+        log("ROUND TRIP FAILED: status %d, equal %s" % (st, same))
+    nc = pc.pc_num_chunks(n, chunk)
+    nsub = pc.pc_num_substreams(n, chunk)
+    cbits = enc.chunk_bits.cpu().numpy().view(np.uint32).astype(np.int64)
+    cwo = enc.chunk_word_offset.cpu().numpy().view(np.uint64)
+    words = int(cwo[nc])
+    payload_bits = int(cbits.sum())
+    xcounts = pc.pc_histogram(x).cpu().numpy().astype(np.float64)
+    p = xcounts[xcounts > 0] / n
+    H = float(-(p * np.log2(p)).sum())
+    shard_blob = pc.pc_codebook_build(xcounts.astype(np.uint64), "huffman")
+    shard_len = pc.codebook_fields(shard_blob)["length"].astype(np.float64)
+    shard_bits = float((xcounts * shard_len).sum()) / n
+    b_payload = payload_bits / n
+    b_total = (words * 32 + 32 * nsub + 96 * nc) / n
+
+    # ---- roofline of the slower kernel --------------------------------
+    payload_bytes = words * 4
+    side_bytes = 4 * nsub + 12 * nc + 8
+    alg = {"encode": n + payload_bytes + side_bytes, "decode": payload_bytes + side_bytes + n}
+    avg = {"encode": sum(enc_ms) / len(enc_ms), "decode": sum(dec_ms) / len(dec_ms)}
+    dom = max(avg, key=avg.get)
+    achieved = alg[dom] / (avg[dom] * 1e-3) / 1e9
+    traffic = load_traffic(dom)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
+                "algorithmic_bytes": alg[dom], "avg_ms": round(avg[dom], 4)}
+    other = "decode" if dom == "encode" else "encode"
+    other_ach = alg[other] / (avg[other] * 1e-3) / 1e9
+
+    # ---- CPU baseline (oracle), rank 0 at N=1 -------------------------
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(os.cpu_count() or 1, 16)
+        host_streams = {
+            "payload": lambda m: enc.payload[:m].cpu().numpy().view(np.uint32),
+            "chunk_bits": cbits.astype(np.uint32),
+            "chunk_word_offset": cwo,
+            "sub_off": enc.sub_off.cpu().numpy().view(np.uint32),
+        }
+        log("cpu baseline: oracle on a bounded sample (%d threads)" % threads)
+        cpu, parity = cpu_baseline_leg(x_np, counts_prev, w.kind, w.qlc_bits, chunk, host_streams,
+                                       args.cpu_seconds, threads)
+
+    res = {
+        "metric": "encode+decode GB/s (uncompressed bytes per round trip), 1 MI355X",
+        "value": round(n / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_bytes": n, "chunk": chunk, "codebook": w.kind,
+                   "qlc_bits": list(w.qlc_bits) if w.qlc_bits else None, "decoder": args.decoder,
+                   "description": w.description},
+        "encode_GBps": round(n / (avg["encode"] * 1e-3) / 1e9, 1),
+        "decode_GBps": round(n / (avg["decode"] * 1e-3) / 1e9, 1),
+        "encode_ms": {"mean": round(avg["encode"], 4), "min": round(min(enc_ms), 4), "max": round(max(enc_ms), 4)},
+        "decode_ms": {"mean": round(avg["decode"], 4), "min": round(min(dec_ms), 4), "max": round(max(dec_ms), 4)},
+        "roofline": roofline,
+        "roofline_other": {"kernel": other, "achieved": round(other_ach, 1),
+                           "frac": round(other_ach / HBM_PEAK_GBPS, 4)},
+        "device_copy_GBps": round(copy_GBps, 1),
+        "bits_per_symbol": {"payload": round(b_payload, 5), "with_side_index": round(b_total, 5),
+                            "entropy": round(H, 5), "per_shard_huffman12": round(shard_bits, 5),
+                            "gap_vs_entropy_rel": round(b_payload / H - 1, 5),
+                            "gap_vs_per_shard_rel": round(b_payload / shard_bits - 1, 5),
+                            "compressibility": round(1 - b_payload / 8, 5),
+                            "entropy_compressibility": round(1 - H / 8, 5)},
+        "codebook_id": "%08x" % fields["codebook_id"],
+        "round_trip_ok": bool(st == 0 and same),
+        "cpu_baseline": cpu,
+        "oracle_parity_sample": parity,
+    }
+    print(json.dumps(res), flush=True)
+    return 0 if (st == 0 and same and (parity is None or all(v for k, v in parity.items() if k != "chunks"))) else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

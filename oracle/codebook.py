@@ -321,3 +321,43 @@ def per_shard_lengths(counts, max_len=MAX_LEN):
 def compressibility(bits_per_symbol: float) -> float:
     """Saved fraction of the 8-bit representation: 1 - b/8."""
     return 1.0 - bits_per_symbol / 8.0
+
+
+def qlc_cost(counts, bits) -> int:
+    """Total bits of a histogram under QLC widths ``bits`` (ranked counts)."""
+    lengths, _, _, _ = qlc_code(counts, bits)
+    return coded_bits(counts, lengths)
+
+
+def qlc_optimal_bits_bruteforce(counts):
+    """The plain definition of the best QLC layout: among all 10**8 width
+    vectors (each width 0..9, areas covering 256 ranks) the one of least total
+    bits, ties to the lexicographically smallest vector.  Exhaustive, with
+    numpy evaluating the last four areas of every vector at once."""
+    ranked = [int(counts[s]) for s in qlc_rank(counts)]
+    pre = np.zeros(ALPHABET + 1, dtype=np.int64)
+    pre[1:] = np.cumsum(np.array(ranked, dtype=np.int64))
+    widths = np.arange(10)
+    tail = np.array(list(itertools.product(range(10), repeat=4)), dtype=np.int64)  # lexicographic
+    best = None
+    for head in itertools.product(range(10), repeat=4):
+        start = 0
+        cost_head = 0
+        for b in head:
+            end = min(start + (1 << b), ALPHABET)
+            cost_head += (3 + b) * int(pre[end] - pre[start])
+            start = end
+        st = np.full(len(tail), start, dtype=np.int64)
+        cost = np.full(len(tail), cost_head, dtype=np.int64)
+        for k in range(4):
+            b = tail[:, k]
+            end = np.minimum(st + (1 << b), ALPHABET)
+            cost += (3 + b) * (pre[end] - pre[st])
+            st = end
+        cost[st < ALPHABET] = np.iinfo(np.int64).max  # does not cover 256 ranks
+        i = int(np.argmin(cost))  # first minimum = lexicographically smallest tail
+        cand = (int(cost[i]), tuple(head) + tuple(int(v) for v in tail[i]))
+        if best is None or cand[0] < best[0]:
+            best = cand
+    del widths
+    return best[1]

@@ -1,0 +1,374 @@
+// Fixed-codebook encoder for gfx950 ("Single-Stage Huffman Encoder for ML
+// Compression", abstract: every symbol goes through one fixed codebook; the
+// codewords are concatenated and nothing else is sent).
+//
+// One workgroup (256 lanes, 4 waves) encodes one chunk.  Per 4096-symbol
+// tile every lane owns 16 consecutive symbols (one 16-byte load, so a wave
+// reads 1 KiB contiguous):
+//   1. code/length lookup in LDS (the 256-entry codebook is copied to LDS);
+//   2. per-lane bit count, wave64 DPP inclusive scan, LDS combine across the
+//      4 waves -> every lane's bit offset inside the chunk, the tile totals
+//      and the chunk's total bit count;
+//   3. the chunk's word offset in the output comes from a single-pass device
+//      exclusive scan over chunks (decoupled look-back on per-chunk
+//      descriptors), so the chunk is written straight to its final place:
+//      the scan and the compaction of chunk payloads are fused here;
+//   4. each lane packs its codewords (4 symbols -> one <=48-bit group) and
+//      ORs them into LDS-staged 32-bit words MSB first; complete words of
+//      the tile are stored coalesced; the partial last word carries over.
+// The side index (bit offset of every 256th symbol) falls out of step 2.
+#include "pc_internal.h"
+
+namespace pc {
+namespace {
+
+constexpr uint32_t kThreads = 256;
+constexpr uint32_t kSymPerLane = 16;
+constexpr uint32_t kTile = kThreads * kSymPerLane;                // 4096
+constexpr uint32_t kStageWords = kTile * PC_MAX_LEN / 32 + 8;     // 1544
+
+// Look-back descriptor per chunk: state in bits 62..63, word count below.
+constexpr uint64_t kDescAggregate = 1ull << 62;
+constexpr uint64_t kDescInclusive = 2ull << 62;
+constexpr uint64_t kDescValue = (1ull << 62) - 1;
+
+__device__ __forceinline__ uint64_t ld_desc(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_desc(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive prefix (in words) of chunk c over all earlier chunks.  Called by
+// one whole wave.  Chunk c's workgroup got ticket c from an atomic counter,
+// so every earlier chunk's workgroup is already running and will publish.
+// The wait on predecessors is bounded: it always ends once they publish,
+// but should an ordering bug ever leave a predecessor silent, the wave gives
+// up after ~2^20 polls (about a second) and sets bit 32 of workspace word 0 instead of
+// spinning forever.
+constexpr uint32_t kMaxPolls = 1u << 20;
+
+__device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_t lane) {
+    if (c == 0) {
+        if (lane == 0) st_desc(&desc[0], kDescInclusive | words);
+        return 0;
+    }
+    if (lane == 0) st_desc(&desc[c], kDescAggregate | words);
+    uint64_t excl = 0;
+    int64_t idx = (int64_t)c - 1;
+    while (true) {
+        const int64_t j = idx - (int64_t)lane;
+        uint64_t d = kDescInclusive;  // before chunk 0: an inclusive zero
+        bool wait = j >= 0;
+        for (uint32_t polls = 0;; ++polls) {
+            if (wait) {
+                d = ld_desc(&desc[j]);
+                wait = (d >> 62) == 0;
+            }
+            if (!__any(wait)) break;
+            if (polls == kMaxPolls) {
+                if (lane == 0) atomicOr(reinterpret_cast<unsigned long long *>(desc - 1), 1ull << 32);
+                return 0;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const uint64_t inc = __ballot((d >> 62) == 2);
+        const uint32_t stop = inc ? (uint32_t)__ffsll((unsigned long long)inc) - 1 : 63;
+        excl += wave_sum_u64(lane <= stop ? (d & kDescValue) : 0);
+        if (inc) break;
+        idx -= 64;
+    }
+    if (lane == 0) st_desc(&desc[c], kDescInclusive | (excl + words));
+    return excl;
+}
+
+struct Shared {
+    uint16_t code[256];
+    uint8_t len[256];
+    uint32_t wave_tot[16][4];
+    uint32_t misc[4];
+    uint32_t stage[kStageWords];
+};
+
+// Bits of the (at most 16) symbols of one lane; symbols at k >= valid count 0.
+__device__ __forceinline__ uint32_t lane_bits(const uint4 &x, uint32_t valid, const Shared &sh) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t t = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t v = w[q];
+        uint32_t l0 = sh.len[v & 0xFF], l1 = sh.len[(v >> 8) & 0xFF];
+        uint32_t l2 = sh.len[(v >> 16) & 0xFF], l3 = sh.len[v >> 24];
+        if (valid < 16) {
+            l0 = 4 * q + 0 < (int)valid ? l0 : 0;
+            l1 = 4 * q + 1 < (int)valid ? l1 : 0;
+            l2 = 4 * q + 2 < (int)valid ? l2 : 0;
+            l3 = 4 * q + 3 < (int)valid ? l3 : 0;
+        }
+        t += l0 + l1 + l2 + l3;
+    }
+    return t;
+}
+
+// OR the codewords of one lane's symbols into the staging words, starting at
+// bit p (bit 0 = MSB of stage[0]).
+__device__ __forceinline__ void pack_lane(const uint4 &x, uint32_t valid, uint32_t p, Shared &sh) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t v = w[q];
+        const uint32_t s0 = v & 0xFF, s1 = (v >> 8) & 0xFF, s2 = (v >> 16) & 0xFF, s3 = v >> 24;
+        uint32_t c0 = sh.code[s0], c1 = sh.code[s1], c2 = sh.code[s2], c3 = sh.code[s3];
+        uint32_t l0 = sh.len[s0], l1 = sh.len[s1], l2 = sh.len[s2], l3 = sh.len[s3];
+        if (valid < 16) {
+            if (4 * q + 0 >= (int)valid) { c0 = 0; l0 = 0; }
+            if (4 * q + 1 >= (int)valid) { c1 = 0; l1 = 0; }
+            if (4 * q + 2 >= (int)valid) { c2 = 0; l2 = 0; }
+            if (4 * q + 3 >= (int)valid) { c3 = 0; l3 = 0; }
+        }
+        // two pairs of <= 24 bits, then one group of <= 48 bits
+        const uint32_t p01 = (c0 << l1) | c1, n01 = l0 + l1;
+        const uint32_t p23 = (c2 << l3) | c3, n23 = l2 + l3;
+        const uint64_t g = ((uint64_t)p01 << n23) | p23;
+        const uint32_t ng = n01 + n23;
+        if (valid < 16 && ng == 0) continue;
+        // left-align the group in 64 bits, then spread it over 3 words at
+        // bit offset o inside word wi
+        const uint64_t a = g << (64 - ng);
+        const uint32_t hi = (uint32_t)(a >> 32), lo = (uint32_t)a;
+        const uint32_t o = p & 31, wi = p >> 5;
+        atomicOr(&sh.stage[wi], hi >> o);
+        atomicOr(&sh.stage[wi + 1], __builtin_amdgcn_alignbit(hi, lo, o));
+        atomicOr(&sh.stage[wi + 2], __builtin_amdgcn_alignbit(lo, 0u, o));
+        p += ng;
+    }
+}
+
+__device__ __forceinline__ uint4 load_lane(const uint8_t *in, uint64_t base, uint32_t off, uint32_t lenc) {
+    if (off + 16 <= lenc) return *reinterpret_cast<const uint4 *>(in + base + off);
+    uint32_t b[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) b[k] = (off + k < lenc) ? in[base + off + k] : 0u;
+    uint4 x;
+    x.x = b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24;
+    x.y = b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24;
+    x.z = b[8] | b[9] << 8 | b[10] << 16 | b[11] << 24;
+    x.w = b[12] | b[13] << 8 | b[14] << 16 | b[15] << 24;
+    return x;
+}
+
+__device__ __forceinline__ uint32_t lane_valid(uint32_t off, uint32_t lenc) {
+    return off >= lenc ? 0u : (lenc - off >= 16 ? 16u : lenc - off);
+}
+
+// Store the finished words of a tile and reset the staging buffer.
+// Stage word 0 is chunk word `first_word`; bits [tile_begin, tile_end) of the
+// chunk are in the buffer.
+__device__ __forceinline__ void flush_tile(Shared &sh, uint32_t *dst, uint32_t tile_begin, uint32_t tile_end,
+                                           bool last, uint32_t tid) {
+    const uint32_t first_word = tile_begin >> 5;
+    const uint32_t nfull = (tile_end >> 5) - first_word;
+    const uint32_t nstore = last ? ((tile_end + 31) >> 5) - first_word : nfull;
+    for (uint32_t i = tid; i < nstore; i += kThreads) dst[first_word + i] = sh.stage[i];
+    const uint32_t carry = sh.stage[nfull];
+    __syncthreads();
+    for (uint32_t i = tid; i <= nfull; i += kThreads) sh.stage[i] = (i == 0 && !last) ? carry : 0u;
+    __syncthreads();
+}
+
+// Chunk size is at most NT tiles: the chunk's symbols stay in registers
+// between the counting pass and the packing pass (input read from HBM once).
+template <int NT>
+__global__ __launch_bounds__(kThreads) void encode_kernel(
+    const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint64_t n, uint32_t chunk,
+    uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
+    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws) {
+    __shared__ Shared sh;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) sh.misc[0] = atomicAdd(reinterpret_cast<uint32_t *>(ws), 1u);
+    {
+        const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
+        sh.code[tid] = reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid];
+        sh.len[tid] = cbb[kOffLength + tid];
+    }
+    for (uint32_t i = tid; i < kStageWords; i += kThreads) sh.stage[i] = 0;
+    __syncthreads();
+    const uint32_t c = uniform(sh.misc[0]);
+    const uint64_t base = (uint64_t)c * chunk;
+    const uint32_t lenc = (uint32_t)((n - base) < chunk ? (n - base) : chunk);
+    const uint32_t ntiles = (lenc + kTile - 1) / kTile;
+
+    // ---- pass 1: load, count bits, scan -------------------------------
+    uint4 x[NT];
+    uint32_t e[NT];
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+        const uint32_t off = r * kTile + tid * kSymPerLane;
+        uint32_t bits = 0;
+        if (r < (int)ntiles) {
+            x[r] = load_lane(in, base, off, lenc);
+            bits = lane_bits(x[r], lane_valid(off, lenc), sh);
+        } else {
+            x[r] = make_uint4(0, 0, 0, 0);
+        }
+        const uint32_t incl = wave_incl_scan(bits);
+        if (lane == 63) sh.wave_tot[r][wave] = incl;
+        e[r] = incl - bits;
+    }
+    __syncthreads();
+    uint32_t tbeg[NT];
+    uint32_t total = 0;
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+        const uint32_t w0 = sh.wave_tot[r][0], w1 = sh.wave_tot[r][1];
+        const uint32_t w2 = sh.wave_tot[r][2], w3 = sh.wave_tot[r][3];
+        e[r] += (wave > 0 ? w0 : 0) + (wave > 1 ? w1 : 0) + (wave > 2 ? w2 : 0);
+        tbeg[r] = uniform(total);
+        total += w0 + w1 + w2 + w3;
+    }
+    total = uniform(total);
+
+    // ---- device exclusive scan over chunks (decoupled look-back) --------
+    const uint64_t words = (total + 31) >> 5;
+    if (wave == 0) {
+        const uint64_t excl = lookback(ws + 1, c, words, lane);
+        if (lane == 0) {
+            sh.misc[1] = (uint32_t)excl;
+            sh.misc[2] = (uint32_t)(excl >> 32);
+        }
+    }
+    __syncthreads();
+    const uint64_t excl = ((uint64_t)sh.misc[2] << 32) | sh.misc[1];
+    if (tid == 0) {
+        chunk_bits[c] = total;
+        cwo[c] = excl;
+        if (c == num_chunks - 1) cwo[num_chunks] = excl + words;
+    }
+    uint32_t *dst = payload + excl;
+    uint32_t *so = sub_off + (uint64_t)c * (chunk / kSub);
+
+    // ---- pass 2: pack into LDS words and store ------------------------
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+        if (r < (int)ntiles) {
+            const uint32_t off = r * kTile + tid * kSymPerLane;
+            const uint32_t valid = lane_valid(off, lenc);
+            const uint32_t pbit = tbeg[r] + e[r];
+            if ((tid & 15) == 0 && valid) so[off / kSub] = pbit;
+            pack_lane(x[r], valid, (tbeg[r] & 31) + e[r], sh);
+            __syncthreads();
+            const uint32_t tend = (r + 1 < (int)ntiles) ? tbeg[r + 1] : total;
+            flush_tile(sh, dst, tbeg[r], tend, r + 1 == (int)ntiles, tid);
+        }
+    }
+}
+
+// Any chunk size: the counting pass and the packing pass each read the
+// chunk (the second read is served by the caches for moderate chunks).
+__global__ __launch_bounds__(kThreads) void encode_kernel_any(
+    const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint64_t n, uint32_t chunk,
+    uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
+    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws) {
+    __shared__ Shared sh;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) sh.misc[0] = atomicAdd(reinterpret_cast<uint32_t *>(ws), 1u);
+    {
+        const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
+        sh.code[tid] = reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid];
+        sh.len[tid] = cbb[kOffLength + tid];
+    }
+    for (uint32_t i = tid; i < kStageWords; i += kThreads) sh.stage[i] = 0;
+    __syncthreads();
+    const uint32_t c = uniform(sh.misc[0]);
+    const uint64_t base = (uint64_t)c * chunk;
+    const uint32_t lenc = (uint32_t)((n - base) < chunk ? (n - base) : chunk);
+    const uint32_t ntiles = (lenc + kTile - 1) / kTile;
+
+    uint32_t mine = 0;
+    for (uint32_t r = 0; r < ntiles; ++r) {
+        const uint32_t off = r * kTile + tid * kSymPerLane;
+        mine += lane_bits(load_lane(in, base, off, lenc), lane_valid(off, lenc), sh);
+    }
+    const uint32_t wsum = wave_incl_scan(mine);
+    if (lane == 63) sh.wave_tot[0][wave] = wsum;
+    __syncthreads();
+    const uint32_t total = uniform(sh.wave_tot[0][0] + sh.wave_tot[0][1] + sh.wave_tot[0][2] + sh.wave_tot[0][3]);
+    const uint64_t words = (total + 31) >> 5;
+    if (wave == 0) {
+        const uint64_t excl = lookback(ws + 1, c, words, lane);
+        if (lane == 0) {
+            sh.misc[1] = (uint32_t)excl;
+            sh.misc[2] = (uint32_t)(excl >> 32);
+        }
+    }
+    __syncthreads();
+    const uint64_t excl = ((uint64_t)sh.misc[2] << 32) | sh.misc[1];
+    if (tid == 0) {
+        chunk_bits[c] = total;
+        cwo[c] = excl;
+        if (c == num_chunks - 1) cwo[num_chunks] = excl + words;
+    }
+    uint32_t *dst = payload + excl;
+    uint32_t *so = sub_off + (uint64_t)c * (chunk / kSub);
+
+    uint32_t tbeg = 0;
+    for (uint32_t r = 0; r < ntiles; ++r) {
+        const uint32_t off = r * kTile + tid * kSymPerLane;
+        const uint32_t valid = lane_valid(off, lenc);
+        const uint4 x = load_lane(in, base, off, lenc);
+        const uint32_t bits = lane_bits(x, valid, sh);
+        const uint32_t incl = wave_incl_scan(bits);
+        // wave_tot[1] holds this tile's per-wave totals (wave_tot[0] is read
+        // above only before the look-back barrier)
+        if (lane == 63) sh.wave_tot[1][wave] = incl;
+        __syncthreads();
+        const uint32_t w0 = sh.wave_tot[1][0], w1 = sh.wave_tot[1][1];
+        const uint32_t w2 = sh.wave_tot[1][2], w3 = sh.wave_tot[1][3];
+        const uint32_t e = incl - bits + (wave > 0 ? w0 : 0) + (wave > 1 ? w1 : 0) + (wave > 2 ? w2 : 0);
+        const uint32_t tend = uniform(tbeg + w0 + w1 + w2 + w3);
+        if ((tid & 15) == 0 && valid) so[off / kSub] = tbeg + e;
+        pack_lane(x, valid, (tbeg & 31) + e, sh);
+        __syncthreads();
+        flush_tile(sh, dst, tbeg, tend, r + 1 == ntiles, tid);
+        tbeg = tend;
+    }
+}
+
+// Zero the ticket and the look-back descriptors; write the total-word entry
+// for an empty input.
+__global__ void encode_init_kernel(uint64_t *ws, uint64_t ws_words, uint64_t *cwo, int empty) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t k = i; k < ws_words; k += stride) ws[k] = 0;
+    if (empty && i == 0) cwo[0] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, uint32_t chunk,
+                         uint32_t *payload, uint32_t *chunk_bits, uint64_t *cwo, uint32_t *sub_off,
+                         uint64_t *ws, hipStream_t stream) {
+    const uint64_t nc = (n + chunk - 1) / chunk;
+    const uint64_t ws_words = 1 + nc;
+    const uint32_t init_blocks = (uint32_t)((ws_words + 255) / 256 < 1024 ? (ws_words + 255) / 256 : 1024);
+    hipLaunchKernelGGL(encode_init_kernel, dim3(init_blocks ? init_blocks : 1), dim3(256), 0, stream, ws,
+                       ws_words, cwo, n == 0 ? 1 : 0);
+    if (n == 0) return hipGetLastError();
+    const uint32_t tiles = (chunk + kTile - 1) / kTile;
+    const dim3 grid((uint32_t)nc), block(kThreads);
+    if (tiles <= 1)
+        hipLaunchKernelGGL(encode_kernel<1>, grid, block, 0, stream, cb, in, n, chunk, (uint32_t)nc, payload,
+                           chunk_bits, cwo, sub_off, ws);
+    else if (tiles <= 4)
+        hipLaunchKernelGGL(encode_kernel<4>, grid, block, 0, stream, cb, in, n, chunk, (uint32_t)nc, payload,
+                           chunk_bits, cwo, sub_off, ws);
+    else if (tiles <= 16)
+        hipLaunchKernelGGL(encode_kernel<16>, grid, block, 0, stream, cb, in, n, chunk, (uint32_t)nc, payload,
+                           chunk_bits, cwo, sub_off, ws);
+    else
+        hipLaunchKernelGGL(encode_kernel_any, grid, block, 0, stream, cb, in, n, chunk, (uint32_t)nc, payload,
+                           chunk_bits, cwo, sub_off, ws);
+    return hipGetLastError();
+}
+
+}  // namespace pc

@@ -1,0 +1,322 @@
+"""Bit-exact parity of the HIP path with the oracle (needs an MI355X).
+
+Every comparison is element by element: payload words, chunk bit counts,
+chunk word offsets, side index and decoded bytes.  The oracle's codebook (not
+the library's) drives the oracle's encoder, so a codebook mismatch also
+fails here.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import codebook as cb
+from oracle import coder
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import static_codebook_lossless_amd as pc
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def make_book(counts, kind="huffman", bits=None):
+    counts = [int(c) for c in counts]
+    blob = pc.pc_codebook_build(np.array(counts, dtype=np.uint64), kind, bits)
+    oracle_book = cb.codebook(counts, kind, bits)
+    return blob.to(DEV), oracle_book
+
+
+def gpu_encode(dcb, x_np, chunk):
+    x = torch.from_numpy(x_np).to(DEV)
+    enc = pc.pc_encode(dcb, x, chunk)
+    torch.cuda.synchronize()
+    return x, enc
+
+
+def host(enc):
+    nc = pc.pc_num_chunks(enc.n, enc.chunk)
+    cwo = enc.chunk_word_offset.cpu().numpy().view(np.uint64)
+    total = int(cwo[nc]) if enc.n else 0
+    return {
+        "payload": enc.payload[:total].cpu().numpy().view(np.uint32),
+        "chunk_bits": enc.chunk_bits.cpu().numpy().view(np.uint32),
+        "chunk_word_offset": cwo,
+        "sub_off": enc.sub_off.cpu().numpy().view(np.uint32),
+    }
+
+
+def assert_same_stream(got, want):
+    for k in ("chunk_bits", "chunk_word_offset", "sub_off", "payload"):
+        a, b = np.asarray(got[k]), np.asarray(want[k]).astype(np.asarray(got[k]).dtype)
+        assert a.shape == b.shape, (k, a.shape, b.shape)
+        if not np.array_equal(a, b):
+            i = int(np.flatnonzero(a != b)[0])
+            raise AssertionError("%s differs first at %d: %d vs %d" % (k, i, int(a[i]), int(b[i])))
+
+
+def roundtrip(dcb, obook, x_np, chunk, qlc_decoder=False):
+    x, enc = gpu_encode(dcb, x_np, chunk)
+    got = host(enc)
+    want = coder.encode(x_np, obook["lengths"], obook["codes"], chunk, threads=8)
+    assert_same_stream(got, want)
+    out, status = pc.pc_decode(dcb, enc)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(out, x)
+    if qlc_decoder:
+        out2, status2 = pc.pc_decode_qlc(dcb, enc)
+        torch.cuda.synchronize()
+        assert int(status2.item()) == 0
+        assert torch.equal(out2, x)
+    return enc
+
+
+@pytest.mark.parametrize("name", ["normal_1m", "ffn1_act", "gelu_act", "int8_weight"])
+def test_workload_parity(name):
+    w = W.WORKLOADS[name]
+    say("workload parity:", name)
+    x_np = W.make(name, 0)
+    counts = np.zeros(256, dtype=np.int64)
+    for s in w.prev_seeds:
+        counts += np.bincount(W.make(name, s), minlength=256)
+    dcb, obook = make_book(counts, w.kind, w.qlc_bits)
+    roundtrip(dcb, obook, x_np, w.chunk, qlc_decoder=(w.kind == "qlc"))
+
+
+def test_stream_1g_full_size_sampled():
+    """The 1 GiB stream in the benchmark's launch configuration: decoded bytes
+    compared in full, encoder outputs compared with the oracle on sampled
+    chunks, and invariants that hold at any size checked on all chunks."""
+    name = "stream_1g"
+    w = W.WORKLOADS[name]
+    say("stream_1g: generating")
+    prev = W.make(name, 1)
+    counts = np.bincount(prev, minlength=256)
+    del prev
+    dcb, obook = make_book(counts)
+    x_np = W.make(name, 0)
+    say("stream_1g: encode")
+    x, enc = gpu_encode(dcb, x_np, w.chunk)
+    say("stream_1g: decode")
+    out, status = pc.pc_decode(dcb, enc)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(out, x)
+    del out
+    cbits = enc.chunk_bits.cpu().numpy().view(np.uint32).astype(np.int64)
+    cwo = enc.chunk_word_offset.cpu().numpy().view(np.uint64).astype(np.int64)
+    nc = cbits.size
+    assert cwo[0] == 0
+    assert np.array_equal(np.diff(cwo), (cbits + 31) // 32)
+    xc = np.bincount(x_np, minlength=256)
+    assert int(cbits.sum()) == cb.coded_bits(xc, obook["lengths"])
+    rng = np.random.default_rng(0)
+    sample = sorted(set(rng.choice(nc, 48, replace=False).tolist()) | {0, nc - 1})
+    spc = w.chunk // 256
+    say("stream_1g: sampled oracle comparison on", len(sample), "chunks")
+    for c in sample:
+        part = x_np[c * w.chunk:(c + 1) * w.chunk]
+        want = coder.encode(part, obook["lengths"], obook["codes"], w.chunk, threads=1)
+        got_words = enc.payload[int(cwo[c]):int(cwo[c + 1])].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got_words, want["payload"]), c
+        assert int(cbits[c]) == int(want["chunk_bits"][0])
+        got_so = enc.sub_off[c * spc:(c + 1) * spc].cpu().numpy().view(np.uint32)
+        assert np.array_equal(got_so, want["sub_off"]), c
+
+
+def skewed(n, seed):
+    rng = np.random.default_rng(seed)
+    return ((rng.zipf(1.4, n) * 37) % 256).astype(np.uint8)
+
+
+def random_counts(seed):
+    rng = np.random.default_rng(1000 + seed)
+    return (rng.pareto(1.1, 256) * 1000).astype(np.int64)
+
+
+@pytest.mark.parametrize("chunk", [256, 768, 4096, 16384, 65536, 131072])
+def test_edge_sizes(chunk):
+    for kind, bits in (("huffman", None), ("qlc", (1, 3, 3, 3, 3, 5, 6, 7))):
+        dcb, obook = make_book(random_counts(chunk), kind, bits)
+        sizes = sorted({0, 1, 255, 256, 257, chunk - 1, chunk, chunk + 1, 3 * chunk + 100})
+        for n in sizes:
+            say("edge size:", kind, "chunk", chunk, "n", n)
+            x_np = skewed(n, n + chunk)
+            if n == 0:
+                x = torch.empty(0, dtype=torch.uint8, device=DEV)
+                enc = pc.pc_encode(dcb, x, chunk)
+                torch.cuda.synchronize()
+                assert int(enc.chunk_word_offset[0].item()) == 0
+                out, status = pc.pc_decode(dcb, enc)
+                torch.cuda.synchronize()
+                assert out.numel() == 0 and int(status.item()) == 0
+                continue
+            roundtrip(dcb, obook, x_np, chunk, qlc_decoder=(kind == "qlc"))
+
+
+def test_many_chunks_lookback():
+    """Tens of thousands of small chunks: stresses the cross-chunk scan."""
+    dcb, obook = make_book(random_counts(3))
+    x_np = skewed(40000 * 256 + 77, 5)
+    say("lookback stress: 40001 chunks of 256")
+    roundtrip(dcb, obook, x_np, 256)
+
+
+@pytest.mark.parametrize("kind", ["huffman", "qlc"])
+def test_degenerate_data(kind):
+    bits = (1, 3, 3, 3, 3, 5, 6, 7) if kind == "qlc" else None
+    counts = np.zeros(256, dtype=np.int64)
+    counts[:40] = np.arange(40, 0, -1) * 1000  # most byte values never seen
+    dcb, obook = make_book(counts, kind, bits)
+    lengths = np.array(obook["lengths"])
+    cases = {
+        "one_frequent_symbol": np.full(100_000, 0, np.uint8),
+        "one_rare_symbol": np.full(100_000, int(np.argmax(lengths)), np.uint8),
+        "uniform": np.tile(np.arange(256, dtype=np.uint8), 400),
+        "unseen_symbols_only": np.arange(40, 256, dtype=np.uint8).repeat(300),
+    }
+    for cname, x_np in cases.items():
+        say("degenerate:", kind, cname)
+        roundtrip(dcb, obook, x_np, 4096, qlc_decoder=(kind == "qlc"))
+
+
+# --------------------------------------------------------------------------
+# corruption: the decoder's status must agree with the oracle decoder's and
+# nothing outside [0, n) may be written
+# --------------------------------------------------------------------------
+
+def decode_guarded(dcb, enc, payload_words=None, qlc=False):
+    n = enc.n
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    out = buf[guard:guard + n]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    fn = pc.pc_decode_qlc if qlc else pc.pc_decode
+    fn(dcb, enc, payload_words=payload_words, out=out, status=status)
+    torch.cuda.synchronize()
+    assert bool((buf[:guard] == 0xA5).all()) and bool((buf[guard + n:] == 0xA5).all()), "write outside [0, n)"
+    return out.clone(), int(status.item())
+
+
+def modified(enc, **kw):
+    d = enc._asdict()
+    d.update(kw)
+    return pc.Encoded(**d)
+
+
+def oracle_status(enc, obook, payload_words=None):
+    h = host(enc)
+    h["chunk_word_offset"] = enc.chunk_word_offset.cpu().numpy().view(np.uint64)
+    pw = payload_words if payload_words is not None else enc.payload.numel()
+    h["payload"] = enc.payload[:pw].cpu().numpy().view(np.uint32)
+    return coder.decode(h, enc.n, enc.chunk, obook)[1]
+
+
+@pytest.mark.parametrize("kind", ["huffman", "qlc"])
+def test_corruptions_detected(kind):
+    bits = (1, 3, 3, 3, 3, 5, 6, 7) if kind == "qlc" else None
+    dcb, obook = make_book(random_counts(11), kind, bits)
+    chunk = 4096
+    x_np = skewed(20 * chunk + 1000, 2)
+    x, enc = gpu_encode(dcb, x_np, chunk)
+    total = int(enc.chunk_word_offset[-1].item())
+    say("corruption:", kind)
+    cases = []
+    cb2 = enc.chunk_bits.clone()
+    cb2[3] -= 1
+    cases.append(("chunk_bits-1", modified(enc, chunk_bits=cb2), None))
+    cb3 = enc.chunk_bits.clone()
+    cb3[5] += 40
+    cases.append(("chunk_bits+40", modified(enc, chunk_bits=cb3), None))
+    so = enc.sub_off.clone()
+    so[7] += 1
+    cases.append(("sub_off+1", modified(enc, sub_off=so), None))
+    so0 = enc.sub_off.clone()
+    so0[16] = 3  # first sub-stream of chunk 1
+    cases.append(("sub_off[first]!=0", modified(enc, sub_off=so0), None))
+    cw = enc.chunk_word_offset.clone()
+    cw[4] += 1
+    cases.append(("cwo+1", modified(enc, chunk_word_offset=cw), None))
+    cases.append(("short payload", enc, total - 1))
+    for cname, e2, pw in cases:
+        say("  case", cname)
+        _, st = decode_guarded(dcb, e2, pw)
+        assert st == pc.PC_ERR_CORRUPT, cname
+        assert oracle_status(e2, obook, pw) == coder.CORRUPT, cname
+    # random bit flips: status agrees with the oracle; an accepted stream
+    # decodes to what the oracle decodes
+    rng = np.random.default_rng(1)
+    for t in range(24):
+        p2 = enc.payload.clone()
+        i = int(rng.integers(0, total))
+        p2[i] ^= int(np.int32(np.uint32(1 << int(rng.integers(0, 32))).view(np.int32)))
+        e2 = modified(enc, payload=p2)
+        out, st = decode_guarded(dcb, e2, total)
+        ost = oracle_status(e2, obook, total)
+        assert (st == pc.PC_ERR_CORRUPT) == (ost == coder.CORRUPT), (t, st, ost)
+        if st == 0:
+            h = host(e2)
+            want, _ = coder.decode(h, enc.n, chunk, obook)
+            assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_unused_qlc_code_detected():
+    bits = (1, 3, 3, 3, 3, 5, 6, 7)
+    counts = np.arange(256, 0, -1) * 10
+    dcb, obook = make_book(counts, "qlc", bits)
+    data = np.arange(256, dtype=np.uint8).repeat(4)  # byte r has rank r
+    lengths, codes = list(obook["lengths"]), list(obook["codes"])
+    codes_bad = codes[:]
+    codes_bad[255] = (7 << 7) | 127  # unused slot of the last area
+    from tests_helpers import string_encode
+    s = string_encode(list(data), lengths, codes_bad, 1024)
+    enc = pc.Encoded(
+        torch.from_numpy(np.concatenate([s["payload"], np.zeros(4, np.uint32)]).view(np.int32)).to(DEV),
+        torch.from_numpy(s["chunk_bits"].view(np.int32)).to(DEV),
+        torch.from_numpy(s["chunk_word_offset"].view(np.int64)).to(DEV),
+        torch.from_numpy(s["sub_off"].view(np.int32)).to(DEV), data.size, 1024)
+    for q in (False, True):
+        _, st = decode_guarded(dcb, enc, len(s["payload"]), qlc=q)
+        assert st == pc.PC_ERR_CORRUPT
+    assert coder.decode(s, data.size, 1024, obook)[1] == coder.CORRUPT
+
+
+def test_qlc_decoder_rejects_huffman_codebook():
+    dcb, obook = make_book(random_counts(4))
+    x_np = skewed(10000, 1)
+    x, enc = gpu_encode(dcb, x_np, 4096)
+    _, st = decode_guarded(dcb, enc, qlc=True)
+    assert st == pc.PC_ERR_CORRUPT
+
+
+# --------------------------------------------------------------------------
+# device histogram (statistics for the offline codebook build)
+# --------------------------------------------------------------------------
+
+def test_histogram_matches_bincount():
+    rng = np.random.default_rng(3)
+    base = torch.from_numpy(skewed(3_000_017, 9)).to(DEV)
+    for off in (0, 1, 7, 15):
+        for n in (0, 1, 15, 16, 17, 100_000, 3_000_000):
+            say("histogram: offset", off, "n", n)
+            x = base[off:off + n]
+            counts = pc.pc_histogram(x)
+            pc.pc_histogram(x, counts)  # accumulates
+            torch.cuda.synchronize()
+            want = 2 * np.bincount(x.cpu().numpy(), minlength=256)
+            assert np.array_equal(counts.cpu().numpy(), want)
+    del rng
