@@ -25,7 +25,6 @@ namespace {
 constexpr uint32_t kThreads = 256;
 constexpr uint32_t kSymPerLane = 16;
 constexpr uint32_t kTile = kThreads * kSymPerLane;                // 4096
-constexpr uint32_t kStageWords = kTile * PC_MAX_LEN / 32 + 8;     // 1544
 
 // Look-back descriptor per chunk: state in bits 62..63, word count below.
 constexpr uint64_t kDescAggregate = 1ull << 62;
@@ -82,16 +81,21 @@ __device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_
     return excl;
 }
 
+template <uint32_t THREADS>
 struct Shared {
+    static constexpr uint32_t kTileSyms = THREADS * kSymPerLane;
+    static constexpr uint32_t kStage = kTileSyms * PC_MAX_LEN / 32 + 8;
     uint16_t code[256];
     uint8_t len[256];
-    uint32_t wave_tot[16][4];
+    uint32_t wave_tot[16][THREADS / 64];  // per tile, per wave: bits (then: bits before the wave)
+    uint32_t tile_beg[17];                // per tile: first bit inside the chunk; [NT] = total
     uint32_t misc[4];
-    uint32_t stage[kStageWords];
+    uint32_t stage[kStage];
 };
 
 // Bits of the (at most 16) symbols of one lane; symbols at k >= valid count 0.
-__device__ __forceinline__ uint32_t lane_bits(const uint4 &x, uint32_t valid, const Shared &sh) {
+template <class SH>
+__device__ __forceinline__ uint32_t lane_bits(const uint4 &x, uint32_t valid, const SH &sh) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
     uint32_t t = 0;
 #pragma unroll
@@ -112,7 +116,8 @@ __device__ __forceinline__ uint32_t lane_bits(const uint4 &x, uint32_t valid, co
 
 // OR the codewords of one lane's symbols into the staging words, starting at
 // bit p (bit 0 = MSB of stage[0]).
-__device__ __forceinline__ void pack_lane(const uint4 &x, uint32_t valid, uint32_t p, Shared &sh) {
+template <class SH>
+__device__ __forceinline__ void pack_lane(const uint4 &x, uint32_t valid, uint32_t p, SH &sh) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -164,102 +169,219 @@ __device__ __forceinline__ uint32_t lane_valid(uint32_t off, uint32_t lenc) {
 // Store the finished words of a tile and reset the staging buffer.
 // Stage word 0 is chunk word `first_word`; bits [tile_begin, tile_end) of the
 // chunk are in the buffer.
-__device__ __forceinline__ void flush_tile(Shared &sh, uint32_t *dst, uint32_t tile_begin, uint32_t tile_end,
+template <uint32_t THREADS, class SH>
+__device__ __forceinline__ void flush_tile(SH &sh, uint32_t *dst, uint32_t tile_begin, uint32_t tile_end,
                                            bool last, uint32_t tid) {
     const uint32_t first_word = tile_begin >> 5;
     const uint32_t nfull = (tile_end >> 5) - first_word;
     const uint32_t nstore = last ? ((tile_end + 31) >> 5) - first_word : nfull;
-    for (uint32_t i = tid; i < nstore; i += kThreads) dst[first_word + i] = sh.stage[i];
+    for (uint32_t i = tid; i < nstore; i += THREADS) dst[first_word + i] = sh.stage[i];
     const uint32_t carry = sh.stage[nfull];
     __syncthreads();
-    for (uint32_t i = tid; i <= nfull; i += kThreads) sh.stage[i] = (i == 0 && !last) ? carry : 0u;
+    for (uint32_t i = tid; i <= nfull; i += THREADS) sh.stage[i] = (i == 0 && !last) ? carry : 0u;
     __syncthreads();
 }
 
-// Chunk size is at most NT tiles: the chunk's symbols stay in registers
-// between the counting pass and the packing pass (input read from HBM once).
-template <int NT>
-__global__ __launch_bounds__(kThreads) void encode_kernel(
+// ---------------------------------------------------------------------------
+// Whole-chunk kernel (chunks of exactly NT tiles of THREADS x 16 symbols).
+//
+// Every symbol is looked up once: the table entry is code | length << 16.
+// Per tile, each lane turns its 16 symbols into 4 groups (<= 48 bits each),
+// the tile's bit offsets come from a wave scan plus a scan of the wave
+// totals, and the groups are ORed straight into an LDS buffer that holds the
+// whole chunk's output.  After the last tile the chunk's size is known; the
+// cross-chunk scan (look-back) gives its word offset and the buffer is stored
+// in one coalesced pass.  A chunk whose output would not fit the buffer
+// (more than BUFW words: only data that does not compress) is redone tile by
+// tile with a store per tile.
+// ---------------------------------------------------------------------------
+
+template <uint32_t THREADS, int NT, uint32_t BUFW>
+struct ChunkShared {
+    uint32_t tab[256];                    // code | length << 16
+    uint32_t wave_tot[NT][THREADS / 64];  // per tile, per wave: bits
+    uint32_t misc[4];
+    uint32_t buf[BUFW + 8];
+};
+
+// Four table entries -> one group: g holds ng bits (right-aligned) once the
+// bits above ng are ignored.  The length field of an entry, shifted along,
+// always lands above the group's valid bits.
+__device__ __forceinline__ void make_group(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3, uint64_t &g,
+                                           uint32_t &ng) {
+    const uint32_t l0 = e0 >> 16, l1 = e1 >> 16, l2 = e2 >> 16, l3 = e3 >> 16;
+    const uint32_t p01 = (e0 << l1) | (e1 & 0xFFFu);
+    const uint32_t n23 = l2 + l3;
+    const uint32_t p23 = __builtin_amdgcn_ubfe((e2 << l3) | (e3 & 0xFFFu), 0, n23);
+    g = ((uint64_t)p01 << n23) | p23;
+    ng = l0 + l1 + n23;
+}
+
+// OR one group (ng bits of g) into the buffer at bit p (bit 0 = MSB of
+// buf[0]); it spans at most 3 words.
+__device__ __forceinline__ void place_group(uint64_t g, uint32_t ng, uint32_t p, uint32_t *buf) {
+    const uint64_t a = g << (64 - ng);
+    const uint32_t hi = (uint32_t)(a >> 32), lo = (uint32_t)a;
+    const uint32_t o = p & 31, wi = p >> 5;
+    atomicOr(&buf[wi], hi >> o);
+    const uint32_t w1 = __builtin_amdgcn_alignbit(hi, lo, o);
+    const uint32_t w2 = __builtin_amdgcn_alignbit(lo, 0u, o);
+    if (w1) atomicOr(&buf[wi + 1], w1);
+    if (w2) atomicOr(&buf[wi + 2], w2);
+}
+
+template <class SH>
+__device__ __forceinline__ void lane_groups(const uint4 &x, const SH &sh, uint64_t g[4], uint32_t ng[4]) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t v = w[q];
+        make_group(sh.tab[v & 0xFF], sh.tab[(v >> 8) & 0xFF], sh.tab[(v >> 16) & 0xFF], sh.tab[v >> 24], g[q],
+                   ng[q]);
+    }
+}
+
+// Bits of tile r before this lane, and the tile's total (both from the
+// per-wave totals the tile just published).
+template <uint32_t NW>
+__device__ __forceinline__ void tile_offsets(const uint32_t *wave_tot, uint32_t lane, uint32_t wave,
+                                             uint32_t &before, uint32_t &total) {
+    const uint32_t v = lane < NW ? wave_tot[lane] : 0u;
+    const uint32_t vs = wave_incl_scan(v);
+    before = wave ? (uint32_t)__builtin_amdgcn_readlane((int)vs, (int)wave - 1) : 0u;
+    total = (uint32_t)__builtin_amdgcn_readlane((int)vs, (int)NW - 1);
+}
+
+template <uint32_t THREADS, int NT, uint32_t BUFW>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS == 1024 ? 8 : 1))) void encode_chunk_kernel(
     const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint64_t n, uint32_t chunk,
     uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
     uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws) {
-    __shared__ Shared sh;
+    using SH = ChunkShared<THREADS, NT, BUFW>;
+    constexpr uint32_t TILE = THREADS * kSymPerLane;
+    constexpr uint32_t NW = THREADS / 64;
+    __shared__ SH sh;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) sh.misc[0] = atomicAdd(reinterpret_cast<uint32_t *>(ws), 1u);
-    {
+    if (tid < 256) {
         const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
-        sh.code[tid] = reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid];
-        sh.len[tid] = cbb[kOffLength + tid];
+        sh.tab[tid] = reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid] | ((uint32_t)cbb[kOffLength + tid] << 16);
     }
-    for (uint32_t i = tid; i < kStageWords; i += kThreads) sh.stage[i] = 0;
+    for (uint32_t i = tid; i < (BUFW + 8) / 4; i += THREADS) reinterpret_cast<uint4 *>(sh.buf)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
     const uint32_t c = uniform(sh.misc[0]);
     const uint64_t base = (uint64_t)c * chunk;
-    const uint32_t lenc = (uint32_t)((n - base) < chunk ? (n - base) : chunk);
-    const uint32_t ntiles = (lenc + kTile - 1) / kTile;
+    const uint8_t *src = in + base + tid * 16;
+    uint32_t *so = sub_off + (uint64_t)c * (chunk / kSub);
 
-    // ---- pass 1: load, count bits, scan -------------------------------
-    uint4 x[NT];
-    uint32_t e[NT];
+    // ---- one pass: lookups, offsets, packing into the chunk buffer -------
+    // (the next tile's 16 bytes are in flight while a tile is processed)
+    uint32_t tbase = 0;
+    bool fits = true;
+    uint4 xn = load_stream16(src);
 #pragma unroll
     for (int r = 0; r < NT; ++r) {
-        const uint32_t off = r * kTile + tid * kSymPerLane;
-        uint32_t bits = 0;
-        if (r < (int)ntiles) {
-            x[r] = load_lane(in, base, off, lenc);
-            bits = lane_bits(x[r], lane_valid(off, lenc), sh);
-        } else {
-            x[r] = make_uint4(0, 0, 0, 0);
-        }
+        const uint4 xc = xn;
+        if (r + 1 < NT) xn = load_stream16(src + (r + 1) * TILE);
+        uint64_t g[4];
+        uint32_t ng[4];
+        lane_groups(xc, sh, g, ng);
+        const uint32_t bits = ng[0] + ng[1] + ng[2] + ng[3];
         const uint32_t incl = wave_incl_scan(bits);
         if (lane == 63) sh.wave_tot[r][wave] = incl;
-        e[r] = incl - bits;
+        __syncthreads();
+        uint32_t before, ttot;
+        tile_offsets<NW>(sh.wave_tot[r], lane, wave, before, ttot);
+        const uint32_t my = tbase + before + incl - bits;
+        if ((tid & 15) == 0) so[(r * TILE + tid * kSymPerLane) / kSub] = my;
+        if (tbase + ttot + 64 > BUFW * 32) {
+            fits = false;
+            break;
+        }
+        uint32_t p = my;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            place_group(g[q], ng[q], p, sh.buf);
+            p += ng[q];
+        }
+        tbase = uniform(tbase + ttot);
     }
-    __syncthreads();
-    uint32_t tbeg[NT];
-    uint32_t total = 0;
+
+    if (fits) {
+        const uint32_t total = tbase;
+        const uint64_t words = (total + 31) >> 5;
+        __syncthreads();
+        if (wave == 0) {
+            const uint64_t excl = lookback(ws + 1, c, words, lane);
+            if (lane == 0) {
+                sh.misc[1] = (uint32_t)excl;
+                sh.misc[2] = (uint32_t)(excl >> 32);
+                chunk_bits[c] = total;
+                cwo[c] = excl;
+                if (c == num_chunks - 1) cwo[num_chunks] = excl + words;
+            }
+        }
+        __syncthreads();
+        uint32_t *dst = payload + (((uint64_t)sh.misc[2] << 32) | sh.misc[1]);
+        for (uint32_t i = tid; i < words; i += THREADS) dst[i] = sh.buf[i];
+        return;
+    }
+
+    // ---- the chunk does not fit: offsets of all tiles, then tile by tile --
+    uint32_t tb[NT + 1], e[NT];
+    tb[0] = 0;
 #pragma unroll
     for (int r = 0; r < NT; ++r) {
-        const uint32_t w0 = sh.wave_tot[r][0], w1 = sh.wave_tot[r][1];
-        const uint32_t w2 = sh.wave_tot[r][2], w3 = sh.wave_tot[r][3];
-        e[r] += (wave > 0 ? w0 : 0) + (wave > 1 ? w1 : 0) + (wave > 2 ? w2 : 0);
-        tbeg[r] = uniform(total);
-        total += w0 + w1 + w2 + w3;
+        uint64_t g[4];
+        uint32_t ng[4];
+        lane_groups(*reinterpret_cast<const uint4 *>(src + r * TILE), sh, g, ng);
+        const uint32_t bits = ng[0] + ng[1] + ng[2] + ng[3];
+        const uint32_t incl = wave_incl_scan(bits);
+        __syncthreads();  // earlier readers of wave_tot[r] are done
+        if (lane == 63) sh.wave_tot[r][wave] = incl;
+        __syncthreads();
+        uint32_t before, ttot;
+        tile_offsets<NW>(sh.wave_tot[r], lane, wave, before, ttot);
+        e[r] = before + incl - bits;
+        tb[r + 1] = uniform(tb[r] + ttot);
+        if ((tid & 15) == 0) so[(r * TILE + tid * kSymPerLane) / kSub] = tb[r] + e[r];
     }
-    total = uniform(total);
-
-    // ---- device exclusive scan over chunks (decoupled look-back) --------
+    const uint32_t total = tb[NT];
     const uint64_t words = (total + 31) >> 5;
+    for (uint32_t i = tid; i < (BUFW + 8) / 4; i += THREADS) reinterpret_cast<uint4 *>(sh.buf)[i] = make_uint4(0, 0, 0, 0);
     if (wave == 0) {
         const uint64_t excl = lookback(ws + 1, c, words, lane);
         if (lane == 0) {
             sh.misc[1] = (uint32_t)excl;
             sh.misc[2] = (uint32_t)(excl >> 32);
+            chunk_bits[c] = total;
+            cwo[c] = excl;
+            if (c == num_chunks - 1) cwo[num_chunks] = excl + words;
         }
     }
     __syncthreads();
-    const uint64_t excl = ((uint64_t)sh.misc[2] << 32) | sh.misc[1];
-    if (tid == 0) {
-        chunk_bits[c] = total;
-        cwo[c] = excl;
-        if (c == num_chunks - 1) cwo[num_chunks] = excl + words;
-    }
-    uint32_t *dst = payload + excl;
-    uint32_t *so = sub_off + (uint64_t)c * (chunk / kSub);
-
-    // ---- pass 2: pack into LDS words and store ------------------------
+    uint32_t *dst = payload + (((uint64_t)sh.misc[2] << 32) | sh.misc[1]);
 #pragma unroll
     for (int r = 0; r < NT; ++r) {
-        if (r < (int)ntiles) {
-            const uint32_t off = r * kTile + tid * kSymPerLane;
-            const uint32_t valid = lane_valid(off, lenc);
-            const uint32_t pbit = tbeg[r] + e[r];
-            if ((tid & 15) == 0 && valid) so[off / kSub] = pbit;
-            pack_lane(x[r], valid, (tbeg[r] & 31) + e[r], sh);
-            __syncthreads();
-            const uint32_t tend = (r + 1 < (int)ntiles) ? tbeg[r + 1] : total;
-            flush_tile(sh, dst, tbeg[r], tend, r + 1 == (int)ntiles, tid);
+        uint64_t g[4];
+        uint32_t ng[4];
+        lane_groups(*reinterpret_cast<const uint4 *>(src + r * TILE), sh, g, ng);
+        uint32_t p = (tb[r] & 31) + e[r];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            place_group(g[q], ng[q], p, sh.buf);
+            p += ng[q];
         }
+        __syncthreads();
+        const uint32_t first_word = tb[r] >> 5;
+        const bool last = r + 1 == NT;
+        const uint32_t nfull = (tb[r + 1] >> 5) - first_word;
+        const uint32_t nstore = last ? ((tb[r + 1] + 31) >> 5) - first_word : nfull;
+        for (uint32_t i = tid; i < nstore; i += THREADS) dst[first_word + i] = sh.buf[i];
+        const uint32_t carry = sh.buf[nfull];
+        __syncthreads();
+        for (uint32_t i = tid; i <= nfull + 2; i += THREADS) sh.buf[i] = (i == 0 && !last) ? carry : 0u;
+        __syncthreads();
     }
 }
 
@@ -269,7 +391,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint64_t n, uint32_t chunk,
     uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
     uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws) {
-    __shared__ Shared sh;
+    using SH = Shared<kThreads>;
+    __shared__ SH sh;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) sh.misc[0] = atomicAdd(reinterpret_cast<uint32_t *>(ws), 1u);
     {
@@ -277,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
         sh.code[tid] = reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid];
         sh.len[tid] = cbb[kOffLength + tid];
     }
-    for (uint32_t i = tid; i < kStageWords; i += kThreads) sh.stage[i] = 0;
+    for (uint32_t i = tid; i < SH::kStage; i += kThreads) sh.stage[i] = 0;
     __syncthreads();
     const uint32_t c = uniform(sh.misc[0]);
     const uint64_t base = (uint64_t)c * chunk;
@@ -329,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
         if ((tid & 15) == 0 && valid) so[off / kSub] = tbeg + e;
         pack_lane(x, valid, (tbeg & 31) + e, sh);
         __syncthreads();
-        flush_tile(sh, dst, tbeg, tend, r + 1 == ntiles, tid);
+        flush_tile<kThreads>(sh, dst, tbeg, tend, r + 1 == ntiles, tid);
         tbeg = tend;
     }
 }
@@ -354,20 +477,31 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
     hipLaunchKernelGGL(encode_init_kernel, dim3(init_blocks ? init_blocks : 1), dim3(256), 0, stream, ws,
                        ws_words, cwo, n == 0 ? 1 : 0);
     if (n == 0) return hipGetLastError();
-    const uint32_t tiles = (chunk + kTile - 1) / kTile;
-    const dim3 grid((uint32_t)nc), block(kThreads);
-    if (tiles <= 1)
-        hipLaunchKernelGGL(encode_kernel<1>, grid, block, 0, stream, cb, in, n, chunk, (uint32_t)nc, payload,
-                           chunk_bits, cwo, sub_off, ws);
-    else if (tiles <= 4)
-        hipLaunchKernelGGL(encode_kernel<4>, grid, block, 0, stream, cb, in, n, chunk, (uint32_t)nc, payload,
-                           chunk_bits, cwo, sub_off, ws);
-    else if (tiles <= 16)
-        hipLaunchKernelGGL(encode_kernel<16>, grid, block, 0, stream, cb, in, n, chunk, (uint32_t)nc, payload,
-                           chunk_bits, cwo, sub_off, ws);
-    else
-        hipLaunchKernelGGL(encode_kernel_any, grid, block, 0, stream, cb, in, n, chunk, (uint32_t)nc, payload,
-                           chunk_bits, cwo, sub_off, ws);
+    const uint64_t nfull = n / chunk;           // chunks of exactly `chunk` symbols
+    const bool short_last = nfull != nc;
+    const dim3 grid((uint32_t)nfull);
+#define PC_ENC(T, NT, BW)                                                                                  \
+    hipLaunchKernelGGL((encode_chunk_kernel<T, NT, BW>), grid, dim3(T), 0, stream, cb, in, n, chunk,         \
+                       (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws)
+    // Chunks of 1, 2 or 4 tiles of 16K symbols use 1024-lane workgroups, 4K
+    // and 8K symbol chunks 256 lanes.  The LDS output buffer holds a whole
+    // chunk at 12 bits per symbol, except for 64K chunks (8 bits per symbol,
+    // so that two workgroups fit in a CU).  Any other chunk size, and a short
+    // last chunk (launched after the full ones, so its look-back finds its
+    // predecessor finished), go to the re-reading kernel.
+    bool fast = true;
+    if (nfull == 0) fast = false;
+    else if (chunk == 65536) PC_ENC(1024, 4, 16384);
+    else if (chunk == 32768) PC_ENC(1024, 2, 12288);
+    else if (chunk == 16384) PC_ENC(1024, 1, 6144);
+    else if (chunk == 8192) PC_ENC(256, 2, 3072);
+    else if (chunk == 4096) PC_ENC(256, 1, 1536);
+    else fast = false;
+    const uint64_t rest = fast ? (short_last ? 1 : 0) : nc;
+    if (rest)
+        hipLaunchKernelGGL(encode_kernel_any, dim3((uint32_t)rest), dim3(kThreads), 0, stream, cb, in, n, chunk,
+                           (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws);
+#undef PC_ENC
     return hipGetLastError();
 }
 

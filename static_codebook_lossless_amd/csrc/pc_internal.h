@@ -69,6 +69,14 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     return v;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load of data read once (non-temporal: not kept in the caches).
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
