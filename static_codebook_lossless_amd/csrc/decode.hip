@@ -11,19 +11,22 @@
 // workgroup decodes group k out of LDS, the loads of group k+1 (its
 // container entries and its payload span, into registers) are in flight, so
 // HBM latency is hidden behind decoding.  Per group:
-//   1. the staged span sits in LDS in rows of 34 words: 32 payload words plus
-//      copies of the next row's first two, so any 3-word window read stays in
-//      one row, and lanes whose sub-streams start ~50 words apart spread over
-//      the LDS banks instead of falling on a few;
-//   2. per lane and per 4 symbols: fetch 3 words at the current bit, funnel
-//      them into a 64-bit window (>= 64 valid bits), then 4 times: read the
-//      16-bit table entry (length | symbol << 8) at the top 12 window bits and
-//      shift the window by the length;
+//   1. the staged span sits in LDS in rows of 36 words: 32 payload words plus
+//      copies of the next row's first four, so any 4-word window read stays
+//      in one row, rows start 16-byte aligned, and lanes whose sub-streams
+//      start ~50 words apart spread over the LDS banks instead of falling on
+//      a few;
+//   2. per lane and per 8 symbols: fetch 4 words at the current bit, funnel
+//      them into a 96-bit window (>= 96 valid bits), then 8 times: read the
+//      16-bit table entry ((32 - length) | symbol << 8) at the top 12 window
+//      bits and advance the window with two funnel shifts (v_alignbit) whose
+//      shift count is the entry itself (the instruction reads 5 bits);
 //   3. 16 decoded bytes per lane go out as one 16-byte store;
 //   4. the sub-stream must end exactly at the next sub-stream's first bit (or
 //      at chunk_bits); any mismatch sets *status = PC_ERR_CORRUPT.
-// A group whose span does not fit the LDS budget is decoded from global
-// memory directly.  The QLC variant replaces the 12-bit table with the
+// A group whose span does not fit the LDS budget is left to a second kernel
+// that decodes it straight from global memory (only data that barely
+// compresses produces such groups).  The QLC variant replaces the 12-bit table with the
 // page's own decoder: a 3-bit area number, that area's fixed-width index, and
 // the 256-entry rank -> symbol table.
 #include "pc_internal.h"
@@ -33,101 +36,112 @@ namespace {
 
 constexpr uint32_t kThreads = 256;
 constexpr uint32_t kRow = 32;     // payload words per LDS row
-constexpr uint32_t kRowPad = 34;  // row + copies of the next row's first 2 words
-// Largest staged span: 56 KiB of payload (14 x 16 B per lane in flight).
-constexpr uint32_t kPrefetch = 14;
-constexpr uint32_t kMaxStageWords = kPrefetch * 4 * kThreads;  // 14336
+constexpr uint32_t kRowPad = 36;  // row + copies of the next row's first 4 words
+// Staged span: up to 64 KiB of payload (8 bits per symbol; 16 x 16 B per
+// lane in flight), so that two workgroups fit in a CU's LDS.
+constexpr uint32_t kPrefetch = 16;
+constexpr uint32_t kMaxStageWords = kPrefetch * 4 * kThreads;  // 16384
+constexpr uint32_t kStageRows = 508;
+static_assert(kStageRows * kRow <= kMaxStageWords, "prefetch covers the staged span");
 constexpr uint32_t kGroupsPerCU = 2;
 
 __device__ __forceinline__ void flag_corrupt(uint32_t *status) {
     atomicCAS(status, 0u, (uint32_t)PC_ERR_CORRUPT);
 }
 
-__device__ __forceinline__ uint32_t row_index(uint32_t a) { return a + 2 * (a >> 5); }
+__device__ __forceinline__ uint32_t row_index(uint32_t a) { return a + 4 * (a >> 5); }
 
 // Payload word sources.  Indices are clamped so that corrupt positions never
 // read outside the staged words or the payload.
 struct LdsWords {
     const uint32_t *w;
     uint32_t last;  // last staged word (relative)
-    __device__ __forceinline__ void fetch3(uint32_t a, uint32_t &w0, uint32_t &w1, uint32_t &w2) const {
+    __device__ __forceinline__ void fetch4(uint32_t a, uint32_t (&v)[4]) const {
         a = a < last ? a : last;
         const uint32_t i = row_index(a);
-        w0 = w[i];
-        w1 = w[i + 1];
-        w2 = w[i + 2];
+        v[0] = w[i];
+        v[1] = w[i + 1];
+        v[2] = w[i + 2];
+        v[3] = w[i + 3];
     }
 };
 
 struct GlobalWords {
     const uint32_t *w;  // payload + wbase
     uint64_t last;      // last readable index relative to w
-    __device__ __forceinline__ void fetch3(uint32_t a, uint32_t &w0, uint32_t &w1, uint32_t &w2) const {
-        const uint64_t i0 = a < last ? a : last;
-        const uint64_t i1 = a + 1 < last ? a + 1 : last;
-        const uint64_t i2 = a + 2 < last ? a + 2 : last;
-        w0 = w[i0];
-        w1 = w[i1];
-        w2 = w[i2];
+    __device__ __forceinline__ void fetch4(uint32_t a, uint32_t (&v)[4]) const {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = w[(uint64_t)a + k < last ? (uint64_t)a + k : last];
     }
 };
 
 struct Tables {
-    const uint16_t *lut;   // LDS: 4096 x (length | symbol << 8), length 0 = no codeword
+    const uint16_t *lut;   // LDS: 4096 x ((32 - length) | symbol << 8), 0 = no codeword
     const uint8_t *sym;    // LDS: sym_of_rank[256] (QLC mode)
     const uint32_t *area;  // LDS: per area (index bits | first rank << 8) (QLC mode)
 };
 
-// Decode 4 symbols from the 64-bit window; returns them packed little-endian.
-// Symbols at index >= lim (masked variant only) consume nothing.
+// Decode 8 symbols from the 96-bit window (h, m, l); returns them packed
+// little-endian in two words and adds the bits consumed to pos.  Symbols at
+// index >= lim (masked variant only) consume nothing.
 template <int MODE, bool MASKED, bool CHECK>
-__device__ __forceinline__ uint32_t decode4(uint64_t win, uint32_t &pos, uint32_t &bad, const Tables &t,
-                                            uint32_t k0, uint32_t lim) {
-    uint32_t e[4];
+__device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint32_t &pos, uint32_t &bad,
+                                        const Tables &t, uint32_t k0, uint32_t lim, uint32_t &o0, uint32_t &o1) {
+    uint32_t e[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t hi = (uint32_t)(win >> 32);
+    for (int k = 0; k < 8; ++k) {
         uint32_t ek, inv;
         if (MODE == kDecodeLut12) {
-            ek = t.lut[hi >> (32 - kPeek)];
+            ek = t.lut[h >> (32 - kPeek)];
             inv = (ek & 0xFF) == 0;
         } else {
-            const uint32_t a = t.area[hi >> 29];
+            const uint32_t a = t.area[h >> 29];
             const uint32_t b = a & 15;
-            const uint32_t r = (a >> 8) + __builtin_amdgcn_ubfe(hi, 29 - b, b);
+            const uint32_t r = (a >> 8) + __builtin_amdgcn_ubfe(h, 29 - b, b);
             inv = r >= 256;
-            ek = (3 + b) | ((uint32_t)t.sym[r & 255] << 8);
+            ek = (29 - b) | ((uint32_t)t.sym[r & 255] << 8);
         }
         if (MASKED && k0 + k >= lim) {
-            ek &= 0xFF00;  // no length: the window stays
+            ek = (ek & 0xFF00) | 32;  // consumes nothing; the window is kept below
             inv = 0;
         }
         if (CHECK) bad |= inv;
-        // the shift uses the low 6 bits only: the length
-        win <<= (ek & 63);
+        // advance by 32 - (ek & 31) = length bits; v_alignbit reads 5 bits of ek
+        const uint32_t h2 = __builtin_amdgcn_alignbit(h, m, ek);
+        const uint32_t m2 = __builtin_amdgcn_alignbit(m, l, ek);
+        const uint32_t l2 = __builtin_amdgcn_alignbit(l, 0u, ek);
+        if (MASKED && (ek & 0xFF) == 32) {
+            // keep the window
+        } else {
+            h = h2;
+            m = m2;
+            l = l2;
+        }
         e[k] = ek;
     }
-    pos += (e[0] + e[1] + e[2] + e[3]) & 0xFF;  // lengths sum to at most 48
-    const uint32_t lo2 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u);
-    const uint32_t hi2 = __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
-    return lo2 | hi2;
+    // each low byte is 32 - length (32 for a masked symbol): 4 of them < 256
+    const uint32_t s0 = (e[0] + e[1] + e[2] + e[3]) & 0xFF, s1 = (e[4] + e[5] + e[6] + e[7]) & 0xFF;
+    pos += 256 - s0 - s1;
+    o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
+    o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
 }
 
+// Symbols [16 g_begin, 16 g_end) of one sub-stream.
 template <int MODE, bool MASKED, bool CHECK, class Src>
-__device__ __forceinline__ uint32_t decode_lane(const Src &src, uint32_t pos, uint32_t lim, const Tables &t,
-                                                uint8_t *dst, uint32_t &bad) {
+__device__ __forceinline__ uint32_t decode_part(const Src &src, uint32_t pos, uint32_t lim, const Tables &t,
+                                                uint8_t *dst, uint32_t &bad, uint32_t g_begin, uint32_t g_end) {
 #pragma unroll 1
-    for (uint32_t g16 = 0; g16 < kSub / 16; ++g16) {
+    for (uint32_t g16 = g_begin; g16 < g_end; ++g16) {
         uint32_t o[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t w0, w1, w2;
-            src.fetch3(pos >> 5, w0, w1, w2);
-            const uint32_t s = pos & 31;
-            const uint64_t a = (((uint64_t)w0 << 32) | w1) << s;
-            const uint64_t b = (((uint64_t)w1 << 32) | w2) << s;
-            const uint64_t win = (a & 0xFFFFFFFF00000000ull) | (b >> 32);
-            o[q] = decode4<MODE, MASKED, CHECK>(win, pos, bad, t, g16 * 16 + q * 4, lim);
+        for (int q = 0; q < 2; ++q) {
+            uint32_t w[4];
+            src.fetch4(pos >> 5, w);
+            const uint32_t sh = pos & 31;
+            const uint32_t h = (uint32_t)(((((uint64_t)w[0] << 32) | w[1]) << sh) >> 32);
+            const uint32_t m = (uint32_t)(((((uint64_t)w[1] << 32) | w[2]) << sh) >> 32);
+            const uint32_t l = (uint32_t)(((((uint64_t)w[2] << 32) | w[3]) << sh) >> 32);
+            decode8<MODE, MASKED, CHECK>(h, m, l, pos, bad, t, g16 * 16 + q * 8, lim, o[2 * q], o[2 * q + 1]);
         }
         if (!MASKED) {
             *reinterpret_cast<uint4 *>(dst + g16 * 16) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -157,7 +171,7 @@ __device__ __forceinline__ LaneMeta load_meta(uint64_t g, uint64_t num_sub, uint
     LaneMeta m{0, 0, 0, 0, 0, 0, 0};
     if (g < num_sub) {
         const uint32_t spc = chunk / kSub;
-        const uint64_t c = g / spc;
+        const uint64_t c = (uint32_t)g / spc;  // num_sub < 2^32 (checked by the launcher)
         const uint32_t j = (uint32_t)(g - c * spc);
         const uint64_t cbase = c * chunk;
         const uint32_t lenc = (uint32_t)((n - cbase) < chunk ? (n - cbase) : chunk);
@@ -174,21 +188,124 @@ __device__ __forceinline__ LaneMeta load_meta(uint64_t g, uint64_t num_sub, uint
     return m;
 }
 
-// Words [lo, hi) of the payload a group needs, from the first sub-stream's
-// start and the next group's first sub-stream (or the end of the payload).
-// Uniform across the workgroup; every lane later checks its own range.
-__device__ __forceinline__ void group_span(uint64_t grp, uint64_t num_sub, uint32_t chunk, uint64_t num_chunks,
-                                           const uint64_t *cwo, const uint32_t *sub_off, uint64_t payload_words,
-                                           uint64_t &lo, uint64_t &hi) {
+// Words [lo, hi) of the payload a group needs: from the first sub-stream's
+// start to the next group's first sub-stream (or the end of the payload).
+// Every lane loads the same four entries with vector loads (scalar loads
+// would share a wait counter with the LDS reads of the decode loop), and
+// every lane later checks its own range against the span.
+struct SpanEntries {
+    uint64_t w_first, w_next;
+    uint32_t off_first, off_next;
+    uint32_t has_next;
+};
+
+__device__ __forceinline__ uint32_t vgpr_copy(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+__device__ __forceinline__ SpanEntries load_span(uint64_t grp, uint64_t num_sub, uint32_t chunk, uint64_t num_chunks,
+                                                 const uint64_t *cwo, const uint32_t *sub_off) {
     const uint32_t spc = chunk / kSub;
-    const uint64_t g0 = grp * kThreads, g1 = g0 + kThreads;
-    const uint64_t a = cwo[g0 / spc] * 32 + sub_off[g0];
-    const uint64_t b = g1 < num_sub ? cwo[g1 / spc] * 32 + sub_off[g1] : cwo[num_chunks] * 32;
-    lo = a >> 5;
-    hi = (b + 31) >> 5;
+    const uint32_t g0 = vgpr_copy((uint32_t)(grp * kThreads));
+    const uint32_t g1 = g0 + kThreads;
+    SpanEntries e;
+    e.has_next = g1 < num_sub;
+    e.w_first = cwo[g0 / spc];
+    e.off_first = sub_off[g0];
+    e.w_next = e.has_next ? cwo[g1 / spc] : cwo[num_chunks];
+    e.off_next = e.has_next ? sub_off[g1] : 0u;
+    return e;
+}
+
+__device__ __forceinline__ void span_words(const SpanEntries &e, uint64_t payload_words, uint64_t &lo, uint64_t &hi) {
+    const uint64_t a = e.w_first * 32 + e.off_first;
+    const uint64_t b = e.w_next * 32 + e.off_next;
+    lo = uniform64(a >> 5);
+    hi = uniform64((b + 31) >> 5);
     if (lo > payload_words) lo = payload_words;
     if (hi > payload_words) hi = payload_words;
     if (hi < lo) hi = lo;
+}
+
+// Prefetch of a staged span into registers: one 16-byte load per quad of
+// words, unconditional and branch-free (an index past the last whole quad is
+// clamped; such quads are never staged), plus the up to 3 words after the
+// last whole quad as single-word loads.  Nothing is read at or past
+// payload_words.
+struct Prefetch {
+    uint4 q[kPrefetch];
+    uint32_t tail[3];
+};
+
+__device__ __forceinline__ void issue_prefetch(Prefetch &pf, const uint32_t *payload, uint64_t payload_words,
+                                               uint64_t lo, uint64_t hi, uint32_t stage_cap, uint32_t tid) {
+    const uint64_t wb = lo & ~(uint64_t)(kRow - 1);
+    if (hi - wb > stage_cap || payload_words <= wb) return;
+    const uint64_t full_q = (payload_words - wb) / 4;
+    const uint4 *src = reinterpret_cast<const uint4 *>(payload + wb);
+    if (full_q > 0) {
+#pragma unroll
+        for (uint32_t k = 0; k < kPrefetch; ++k) {
+            const uint64_t q = tid + k * kThreads;
+            pf.q[k] = load_stream16(src + (q < full_q ? q : full_q - 1));
+        }
+    }
+#pragma unroll
+    for (uint32_t t = 0; t < 3; ++t) {
+        const uint64_t i = wb + 4 * full_q + t;
+        pf.tail[t] = payload[i < payload_words ? i : payload_words - 1];
+    }
+}
+
+// Tables into LDS (shared by both kernels).
+template <int MODE>
+__device__ __forceinline__ void load_tables(const uint8_t *cbb, uint4 *tab4, uint32_t *area_tab, uint32_t tid) {
+    if (MODE == kDecodeLut12) {
+        // 16-bit entries (32 - length) | symbol << 8 (0: no codeword)
+        const uint8_t *ds = cbb + kOffDecSym, *dl = cbb + kOffDecSym + 4096;
+        uint16_t *lut = reinterpret_cast<uint16_t *>(tab4);
+        for (uint32_t i = tid; i < 4096; i += kThreads) {
+            const uint32_t len = dl[i];
+            lut[i] = (uint16_t)(len ? ((32 - len) | ((uint32_t)ds[i] << 8)) : 0u);
+        }
+    } else {
+        if (tid < 64)
+            reinterpret_cast<uint32_t *>(tab4)[tid] = reinterpret_cast<const uint32_t *>(cbb + kOffSymOfRank)[tid];
+        if (tid < 8) {
+            const uint32_t b = cbb[kOffQlcBits + tid];
+            const uint32_t st = reinterpret_cast<const uint16_t *>(cbb + kOffQlcStart)[tid];
+            area_tab[tid] = b | (st << 8);
+        }
+    }
+}
+
+__device__ __forceinline__ bool span_staged(uint64_t lo, uint64_t hi, uint64_t payload_words, uint32_t stage_cap) {
+    const uint64_t wb = lo & ~(uint64_t)(kRow - 1);
+    return hi - wb <= stage_cap && payload_words > wb;
+}
+
+// Per-lane checks of a sub-stream against its group's span [wbase, hi).
+struct LaneJob {
+    bool ok;
+    uint32_t lim, pos0, pos_want;
+};
+
+__device__ __forceinline__ LaneJob lane_job(const LaneMeta &m, bool kind_ok, uint64_t payload_words, uint64_t wbase,
+                                            uint64_t hi, uint32_t *status) {
+    const uint32_t end = m.end == 0xFFFFFFFFu ? m.cbits : m.end;
+    const uint64_t abs_s = m.w0 * 32 + m.start, abs_e = m.w0 * 32 + end;
+    const bool active = m.lim > 0;
+    LaneJob j;
+    j.ok = active && kind_ok && m.w1 >= m.w0 && (m.w1 - m.w0) == ((uint64_t)m.cbits + 31) / 32 &&
+           m.w1 <= payload_words && (!m.first || m.start == 0) && m.start <= end && end <= m.cbits &&
+           abs_s >= wbase * 32 && abs_e <= hi * 32 && hi - wbase < (1u << 26);
+    if (active && !j.ok) flag_corrupt(status);
+    j.lim = j.ok ? m.lim : 0;
+    j.pos0 = j.ok ? (uint32_t)(abs_s - wbase * 32) : 0;
+    j.pos_want = j.ok ? (uint32_t)(abs_e - wbase * 32) : 0;
+    return j;
 }
 
 template <int MODE>
@@ -206,31 +323,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const uint32_t tid = threadIdx.x;
     const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
     const pc_codebook *cbp = reinterpret_cast<const pc_codebook *>(cb);
-
-    if (MODE == kDecodeLut12) {
-        // interleave dec_len / dec_sym into 16-bit entries
-        for (uint32_t i = tid; i < 256; i += kThreads) {
-            const uint4 s = reinterpret_cast<const uint4 *>(cbb + kOffDecSym)[i];
-            const uint4 l = reinterpret_cast<const uint4 *>(cbb + kOffDecSym + 4096)[i];
-            const uint32_t sv[4] = {s.x, s.y, s.z, s.w}, lv[4] = {l.x, l.y, l.z, l.w};
-            uint32_t o[8];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                o[2 * k] = __builtin_amdgcn_perm(sv[k], lv[k], 0x05010400u);
-                o[2 * k + 1] = __builtin_amdgcn_perm(sv[k], lv[k], 0x07030602u);
-            }
-            tab4[2 * i] = make_uint4(o[0], o[1], o[2], o[3]);
-            tab4[2 * i + 1] = make_uint4(o[4], o[5], o[6], o[7]);
-        }
-    } else {
-        if (tid < 64)
-            reinterpret_cast<uint32_t *>(tab4)[tid] = reinterpret_cast<const uint32_t *>(cbb + kOffSymOfRank)[tid];
-        if (tid < 8) {
-            const uint32_t b = cbb[kOffQlcBits + tid];
-            const uint32_t st = reinterpret_cast<const uint16_t *>(cbb + kOffQlcStart)[tid];
-            area_tab[tid] = b | (st << 8);
-        }
-    }
+    load_tables<MODE>(cbb, tab4, area_tab, tid);
     const bool kind_ok = MODE == kDecodeLut12 || cbp->kind == PC_CODEBOOK_QLC;
     const bool complete = cbp->complete == 1;
     Tables t;
@@ -243,108 +336,127 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     if (grp >= num_groups) return;
     LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
     uint64_t lo, hi;
-    group_span(grp, num_sub, chunk, num_chunks, cwo, sub_off, payload_words, lo, hi);
-    uint4 pre[kPrefetch];
-    auto issue_payload = [&](uint64_t lo_, uint64_t hi_) {
-        const uint64_t wb = lo_ & ~(uint64_t)(kRow - 1);
-        const uint64_t cnt = hi_ - wb;
-        if (cnt <= stage_cap) {
-            const uint32_t nq = (uint32_t)((cnt + 3) / 4);
-            const uint4 *src = reinterpret_cast<const uint4 *>(payload + wb);
-            const uint64_t full_q = (payload_words - wb) / 4;  // 16-byte loads fully inside the payload
-#pragma unroll
-            for (uint32_t k = 0; k < kPrefetch; ++k) {
-                const uint32_t q = tid + k * kThreads;
-                if (q < nq) {
-                    if (q < full_q) {
-                        pre[k] = load_stream16(src + q);
-                    } else {
-                        uint32_t v[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            v[i] = (wb + 4 * q + i < payload_words) ? payload[wb + 4 * q + i] : 0u;
-                        pre[k] = make_uint4(v[0], v[1], v[2], v[3]);
-                    }
-                }
-            }
-        }
-    };
-    issue_payload(lo, hi);
+    span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
+    Prefetch pf;
+    issue_prefetch(pf, payload, payload_words, lo, hi, stage_cap, tid);
 
     for (;;) {
-        // ---- stage the current group (its loads were issued earlier) --
         const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
         const uint64_t cnt = hi - wbase;
-        const bool staged = cnt <= stage_cap;
+        const bool staged = span_staged(lo, hi, payload_words, stage_cap);
+        // ---- stage the current group (its loads were issued earlier) --
         __syncthreads();  // every lane is done with the previous group's rows
         if (staged) {
             const uint32_t nq = (uint32_t)((cnt + 3) / 4);
+            const uint64_t full_q = (payload_words - wbase) / 4;
 #pragma unroll
             for (uint32_t k = 0; k < kPrefetch; ++k) {
                 const uint32_t q = tid + k * kThreads;
-                if (q < nq) {
-                    const uint32_t i = row_index(4 * q);
-                    uint2 *d = reinterpret_cast<uint2 *>(stage + i);
-                    d[0] = make_uint2(pre[k].x, pre[k].y);
-                    d[1] = make_uint2(pre[k].z, pre[k].w);
-                    if ((q & 7) == 0 && q) *reinterpret_cast<uint2 *>(stage + i - 2) = make_uint2(pre[k].x, pre[k].y);
+                if (q < nq && q <= full_q) {
+                    uint32_t v[4] = {pf.q[k].x, pf.q[k].y, pf.q[k].z, pf.q[k].w};
+                    if (q == full_q) {  // the words after the last whole quad
+                        v[0] = pf.tail[0];
+                        v[1] = pf.tail[1];
+                        v[2] = pf.tail[2];
+                        v[3] = 0;
+                    }
+                    const uint32_t i = row_index(4 * q);  // a multiple of 4
+                    const uint4 qv = make_uint4(v[0], v[1], v[2], v[3]);
+                    stage4[i / 4] = qv;
+                    if ((q & 7) == 0 && q) stage4[i / 4 - 1] = qv;  // copies ending the previous row
                 }
             }
         }
         __syncthreads();
 
-        // ---- this lane's checks -----------------------------------------
-        const uint32_t end = meta.end == 0xFFFFFFFFu ? meta.cbits : meta.end;
-        const uint64_t abs_s = meta.w0 * 32 + meta.start, abs_e = meta.w0 * 32 + end;
-        const bool active = meta.lim > 0;
-        const bool ok = active && kind_ok && meta.w1 >= meta.w0 &&
-                        (meta.w1 - meta.w0) == ((uint64_t)meta.cbits + 31) / 32 && meta.w1 <= payload_words &&
-                        (!meta.first || meta.start == 0) && meta.start <= end && end <= meta.cbits &&
-                        abs_s >= wbase * 32 && abs_e <= hi * 32 && cnt < (1u << 26);
-        if (active && !ok) flag_corrupt(status);
-        const uint32_t lim = ok ? meta.lim : 0;
-        const uint32_t pos0 = ok ? (uint32_t)(abs_s - wbase * 32) : 0;
-        const uint32_t pos_want = ok ? (uint32_t)(abs_e - wbase * 32) : 0;
-        uint8_t *dst = out + (grp * kThreads + tid) * kSub;
-        const bool allfull = __syncthreads_count(lim == kSub) == (int)kThreads;
-
-        // ---- issue the next group's loads ------------------------------
+        // ---- the next group's entries (its payload: halfway through) ----
         const uint64_t nxt = grp + gridDim.x;
         const bool more = nxt < num_groups;
-        uint64_t nlo = 0, nhi = 0;
         LaneMeta nmeta{0, 0, 0, 0, 0, 0, 0};
+        SpanEntries nspan{0, 0, 0, 0, 0};
         if (more) {
             nmeta = load_meta(nxt * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
-            group_span(nxt, num_sub, chunk, num_chunks, cwo, sub_off, payload_words, nlo, nhi);
-            issue_payload(nlo, nhi);
+            nspan = load_span(nxt, num_sub, chunk, num_chunks, cwo, sub_off);
         }
-
-        // ---- decode --------------------------------------------------
-        uint32_t bad = 0, pos_end = 0;
+        // ---- decode: first half, the next group's payload loads, second half
+        uint64_t nlo = 0, nhi = 0;
+        LaneJob job{false, 0, 0, 0};
+        int variant = 0;  // 0: all lanes owe 256 symbols, complete code; 1: same, check codes; 2: masked
+        uint8_t *dst = out + (grp * kThreads + tid) * kSub;
+        LdsWords src{stage, (uint32_t)(cnt > 0 ? cnt - 1 : 0)};
+        uint32_t bad = 0, pos = 0;
         if (staged) {
-            LdsWords src{stage, (uint32_t)(cnt > 0 ? cnt - 1 : 0)};
-            if (allfull) {
-                if (complete)
-                    pos_end = decode_lane<MODE, false, false>(src, pos0, lim, t, dst, bad);
-                else
-                    pos_end = decode_lane<MODE, false, true>(src, pos0, lim, t, dst, bad);
-            } else if (active) {
-                pos_end = decode_lane<MODE, true, true>(src, pos0, lim, t, dst, bad);
-            }
-        } else if (cnt > 0) {
-            GlobalWords src{payload + wbase, cnt - 1};
-            if (allfull)
-                pos_end = decode_lane<MODE, false, true>(src, pos0, lim, t, dst, bad);
-            else if (active)
-                pos_end = decode_lane<MODE, true, true>(src, pos0, lim, t, dst, bad);
+            job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
+            const bool allfull = __syncthreads_count(job.lim == kSub) == (int)kThreads;
+            variant = allfull ? (complete ? 0 : 1) : 2;
+            pos = job.pos0;
+            if (variant == 0)
+                pos = decode_part<MODE, false, false>(src, pos, job.lim, t, dst, bad, 0, kSub / 32);
+            else if (variant == 1)
+                pos = decode_part<MODE, false, true>(src, pos, job.lim, t, dst, bad, 0, kSub / 32);
+            else
+                pos = decode_part<MODE, true, true>(src, pos, job.lim, t, dst, bad, 0, kSub / 32);
         }
-        if (ok && (bad || pos_end != pos_want)) flag_corrupt(status);
+        if (more) {
+            span_words(nspan, payload_words, nlo, nhi);
+            issue_prefetch(pf, payload, payload_words, nlo, nhi, stage_cap, tid);
+        }
+        if (staged) {
+            if (variant == 0)
+                pos = decode_part<MODE, false, false>(src, pos, job.lim, t, dst, bad, kSub / 32, kSub / 16);
+            else if (variant == 1)
+                pos = decode_part<MODE, false, true>(src, pos, job.lim, t, dst, bad, kSub / 32, kSub / 16);
+            else
+                pos = decode_part<MODE, true, true>(src, pos, job.lim, t, dst, bad, kSub / 32, kSub / 16);
+            if (job.ok && (bad || pos != job.pos_want)) flag_corrupt(status);
+        }
 
         if (!more) break;
         grp = nxt;
         meta = nmeta;
         lo = nlo;
         hi = nhi;
+    }
+}
+
+// Groups whose span exceeds the LDS budget, decoded from global memory (the
+// same span test as the main kernel picks them; each lane reads its words
+// directly).  Grid-stride over all groups.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void decode_global_kernel(
+    const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
+    const uint32_t *__restrict__ chunk_bits, const uint64_t *__restrict__ cwo,
+    const uint32_t *__restrict__ sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub, uint64_t num_groups,
+    uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status, uint32_t stage_cap) {
+    __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 16];
+    __shared__ uint32_t area_tab[8];
+    const uint32_t tid = threadIdx.x;
+    const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
+    const pc_codebook *cbp = reinterpret_cast<const pc_codebook *>(cb);
+    bool loaded = false;
+    const bool kind_ok = MODE == kDecodeLut12 || cbp->kind == PC_CODEBOOK_QLC;
+    Tables t;
+    t.lut = reinterpret_cast<const uint16_t *>(tab4);
+    t.sym = reinterpret_cast<const uint8_t *>(tab4);
+    t.area = area_tab;
+    for (uint64_t grp = blockIdx.x; grp < num_groups; grp += gridDim.x) {
+        uint64_t lo, hi;
+        span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
+        if (span_staged(lo, hi, payload_words, stage_cap)) continue;  // done by the main kernel
+        if (!loaded) {
+            load_tables<MODE>(cbb, tab4, area_tab, tid);
+            __syncthreads();
+            loaded = true;
+        }
+        const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
+        const LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
+        const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
+        if (payload_words <= wbase) continue;  // nothing readable: every lane was flagged
+        uint8_t *dst = out + (grp * kThreads + tid) * kSub;
+        GlobalWords src{payload + wbase, payload_words - wbase - 1};
+        uint32_t bad = 0;
+        const uint32_t pos_end = decode_part<MODE, true, true>(src, job.pos0, job.lim, t, dst, bad, 0, kSub / 16);
+        if (job.ok && (bad || pos_end != job.pos_want)) flag_corrupt(status);
     }
 }
 
@@ -358,13 +470,12 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     const uint64_t last = n - (nc - 1) * chunk;
     const uint64_t num_sub = (nc - 1) * (chunk / kSub) + (last + kSub - 1) / kSub;
     const uint64_t num_groups = (num_sub + kThreads - 1) / kThreads;
-    // LDS budget for a staged span: the average span of a group plus 1/16
-    // slack and two rows, at most kMaxStageWords; stored as rows of 34 words.
-    const uint64_t avg_words = (payload_words * kThreads + num_sub - 1) / (num_sub ? num_sub : 1);
-    uint64_t cap = avg_words + avg_words / 16 + 2 * kRow;
-    if (cap > kMaxStageWords) cap = kMaxStageWords;
-    cap = (cap + kRow - 1) / kRow * kRow;
-    const size_t shmem = (cap / kRow + 1) * kRowPad * 4;
+    // LDS budget for a staged span: always the largest that lets two
+    // workgroups share a CU's 160 KiB (two per CU is the occupancy the
+    // kernel's registers allow anyway): 508 rows of 36 words beside the 8 KiB
+    // table, i.e. up to 16256 payload words (7.9 bits per symbol).
+    const uint64_t cap = kStageRows * kRow;
+    const size_t shmem = kStageRows * kRowPad * 4;
     static bool attr_set[2] = {false, false};
     static int num_cus = 0;
     if (!num_cus) {
@@ -377,20 +488,28 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
                                           : (const void *)decode_kernel<kDecodeQlc>;
     if (!attr_set[mode]) {
         const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (kMaxStageWords / kRow + 1) * kRowPad * 4);
+                                                 kStageRows * kRowPad * 4);
         if (e != hipSuccess) return e;
         attr_set[mode] = true;
     }
     uint64_t grid = (uint64_t)num_cus * kGroupsPerCU;
     if (grid > num_groups) grid = num_groups;
-    if (mode == kDecodeLut12)
-        hipLaunchKernelGGL(decode_kernel<kDecodeLut12>, dim3((uint32_t)grid), dim3(kThreads), shmem, stream, cb,
-                           payload, payload_words, chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, nc, out,
-                           status, (uint32_t)cap);
-    else
-        hipLaunchKernelGGL(decode_kernel<kDecodeQlc>, dim3((uint32_t)grid), dim3(kThreads), shmem, stream, cb,
-                           payload, payload_words, chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, nc, out,
-                           status, (uint32_t)cap);
+    if (num_sub >= 0xFFFFFFFFull) return hipErrorInvalidValue;
+#define PC_DEC(K)                                                                                             \
+    hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), shmem, stream, cb, payload, payload_words,     \
+                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, nc, out, status, (uint32_t)cap)
+#define PC_DEC_G(K)                                                                                           \
+    hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), 0, stream, cb, payload, payload_words,         \
+                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, nc, out, status, (uint32_t)cap)
+    if (mode == kDecodeLut12) {
+        PC_DEC(decode_kernel<kDecodeLut12>);
+        PC_DEC_G(decode_global_kernel<kDecodeLut12>);
+    } else {
+        PC_DEC(decode_kernel<kDecodeQlc>);
+        PC_DEC_G(decode_global_kernel<kDecodeQlc>);
+    }
+#undef PC_DEC
+#undef PC_DEC_G
     return hipGetLastError();
 }
 

@@ -41,11 +41,15 @@ __device__ __forceinline__ void st_desc(uint64_t *p, uint64_t v) {
 // Exclusive prefix (in words) of chunk c over all earlier chunks.  Called by
 // one whole wave.  Chunk c's workgroup got ticket c from an atomic counter,
 // so every earlier chunk's workgroup is already running and will publish.
+// Each round reads 256 predecessors (4 per lane, nearest first) in one trip
+// to L2, so the walk back to the nearest published inclusive prefix rarely
+// takes more than one round.
 // The wait on predecessors is bounded: it always ends once they publish,
 // but should an ordering bug ever leave a predecessor silent, the wave gives
-// up after ~2^20 polls (about a second) and sets bit 32 of workspace word 0 instead of
-// spinning forever.
+// up after ~2^20 polls (about a second) and sets bit 32 of workspace word 0
+// instead of spinning forever.
 constexpr uint32_t kMaxPolls = 1u << 20;
+constexpr int kLookWin = 4;  // descriptors per lane per round
 
 __device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_t lane) {
     if (c == 0) {
@@ -56,26 +60,43 @@ __device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_
     uint64_t excl = 0;
     int64_t idx = (int64_t)c - 1;
     while (true) {
-        const int64_t j = idx - (int64_t)lane;
-        uint64_t d = kDescInclusive;  // before chunk 0: an inclusive zero
-        bool wait = j >= 0;
+        // window w, lane l looks at chunk idx - (64 w + l)
+        uint64_t d[kLookWin];
+        bool wait[kLookWin];
+#pragma unroll
+        for (int w = 0; w < kLookWin; ++w) {
+            d[w] = kDescInclusive;  // before chunk 0: an inclusive zero
+            wait[w] = idx - (int64_t)(64 * w + lane) >= 0;
+        }
         for (uint32_t polls = 0;; ++polls) {
-            if (wait) {
-                d = ld_desc(&desc[j]);
-                wait = (d >> 62) == 0;
+            bool any = false;
+#pragma unroll
+            for (int w = 0; w < kLookWin; ++w) {
+                if (wait[w]) {
+                    d[w] = ld_desc(&desc[idx - (int64_t)(64 * w + lane)]);
+                    wait[w] = (d[w] >> 62) == 0;
+                }
+                any |= wait[w];
             }
-            if (!__any(wait)) break;
+            if (!__any(any)) break;
             if (polls == kMaxPolls) {
                 if (lane == 0) atomicOr(reinterpret_cast<unsigned long long *>(desc - 1), 1ull << 32);
                 return 0;
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        const uint64_t inc = __ballot((d >> 62) == 2);
-        const uint32_t stop = inc ? (uint32_t)__ffsll((unsigned long long)inc) - 1 : 63;
-        excl += wave_sum_u64(lane <= stop ? (d & kDescValue) : 0);
-        if (inc) break;
-        idx -= 64;
+        bool found = false;
+#pragma unroll
+        for (int w = 0; w < kLookWin; ++w) {
+            if (!found) {
+                const uint64_t inc = __ballot((d[w] >> 62) == 2);
+                const uint32_t stop = inc ? (uint32_t)__ffsll((unsigned long long)inc) - 1 : 63;
+                excl += wave_sum_u64(lane <= stop ? (d[w] & kDescValue) : 0);
+                found = inc != 0;
+            }
+        }
+        if (found) break;
+        idx -= 64 * kLookWin;
     }
     if (lane == 0) st_desc(&desc[c], kDescInclusive | (excl + words));
     return excl;
