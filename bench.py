@@ -31,12 +31,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "coder_kernels_stream_1g_hbm_traffic.txt")
 KERNEL_SOURCES = {
     "encode": os.path.join(ROOT, "static_codebook_lossless_amd", "csrc", "encode.hip"),
     "decode": os.path.join(ROOT, "static_codebook_lossless_amd", "csrc", "decode.hip"),
 }
-KERNEL_NAMES = {"encode": "encode_kernel", "decode": "decode_kernel"}
+KERNEL_NAMES = {"encode": "encode_chunk_kernel", "decode": "decode_kernel<0>"}
 
 
 def log(*a):
@@ -64,24 +64,38 @@ def _read_counter_csv(d, counter):
     with open(files[0]) as f:
         for r in csv.DictReader(f):
             if r.get("Counter_Name") == counter:
-                rows.append((r["Kernel_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id")))
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
     return rows
 
 
 def pmc_summary(fetch_dir, write_dir, copy_bytes, out=TRAFFIC_FILE):
+    """Per-dispatch HBM bytes of the coder kernels.  The plain device copy of
+    copy_bytes bytes that bench.py runs (it reads copy_bytes and writes
+    copy_bytes) calibrates each counter: scale = copy_bytes / counter(copy)."""
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = _read_counter_csv(d, counter)
         per = {}
-        for name, val, _ in rows:
+        for name, val in _read_counter_csv(d, counter):
             per.setdefault(name, []).append(val * 1024.0)  # KiB -> bytes
-        copy_vals = [v for k, vs in per.items() if "copy" in k.lower() or "elementwise" in k.lower() for v in vs]
+        copy_vals = [max(vs) for k, vs in per.items() if "copyBuffer" in k]
         if not copy_vals:
             raise RuntimeError("no copy kernel found for the %s scale" % counter)
-        scale = copy_bytes / (sum(copy_vals) / len(copy_vals))
-        res[counter] = {"scale": scale, "kernels": {k: sum(v) / len(v) for k, v in per.items()}}
-    lines = ["# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of bench.py.",
-             "# Each counter is scaled by copy_bytes / counter(plain copy of copy_bytes bytes).",
+        scale = copy_bytes / max(copy_vals)
+        res[counter] = {"scale": scale, "kernels": {k: sorted(v)[len(v) // 2] for k, v in per.items()}}
+    lines = ["# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of bench.py.",
+             "# Made by (from the repository root, after cd /tmp && export TMPDIR=/tmp):",
+             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o bench -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o bench -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "#   python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             "# Each counter is scaled by copy_bytes / counter(plain device copy of copy_bytes bytes).",
+             "# Raw medians (KiB per dispatch): " + "; ".join(
+                 "%s %s %.1f" % (c, lab, v / 1024.0)
+                 for c in ("FETCH_SIZE", "WRITE_SIZE")
+                 for k, v in res[c]["kernels"].items()
+                 for lab in [next((kn for kn in ["copyBuffer"] + list(KERNEL_NAMES.values()) if kn in k), None)]
+                 if lab),
              "copy_bytes %d" % copy_bytes,
              "fetch_scale %.6f" % res["FETCH_SIZE"]["scale"],
              "write_scale %.6f" % res["WRITE_SIZE"]["scale"]]
@@ -92,6 +106,7 @@ def pmc_summary(fetch_dir, write_dir, copy_bytes, out=TRAFFIC_FILE):
             fb = f[0] * res["FETCH_SIZE"]["scale"]
             wb = w[0] * res["WRITE_SIZE"]["scale"]
             lines.append("kernel %s sha %s fetch_bytes %.0f write_bytes %.0f" % (kind, source_sha(kind), fb, wb))
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -197,7 +212,7 @@ def main():
     if args.pmc_summary:
         import workloads as W
 
-        cb = args.copy_bytes or W.WORKLOADS[args.workload].n * 2
+        cb = args.copy_bytes or W.WORKLOADS[args.workload].n
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], cb)
         return 0
     if args.gpus != 1 or world != 1:
