@@ -21,7 +21,8 @@
 //      16-bit table entry ((32 - length) | symbol << 8) at the top 12 window
 //      bits and advance the window with two funnel shifts (v_alignbit) whose
 //      shift count is the entry itself (the instruction reads 5 bits);
-//   3. 16 decoded bytes per lane go out as one 16-byte store;
+//   3. every 64 decoded bytes of a lane go out as four adjacent 16-byte
+//      stores;
 //   4. the sub-stream must end exactly at the next sub-stream's first bit (or
 //      at chunk_bits); any mismatch sets *status = PC_ERR_CORRUPT.
 // A group whose span does not fit the LDS budget is left to a second kernel
@@ -124,34 +125,58 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
     pos += 256 - s0 - s1;
     o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
     o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
+    // pack here: left to the scheduler, the packing sinks towards the store
+    // and keeps all eight entries of every step alive until then
+    asm volatile("" : "+v"(o0), "+v"(o1));
 }
 
-// Symbols [16 g_begin, 16 g_end) of one sub-stream.
+// Decoded bytes leave a lane in blocks of 64 (full lanes: four adjacent
+// 16-byte stores to one 64-byte segment, so the L2 receives whole segments
+// instead of 16-byte pieces of lines that other stores complete much later)
+// or of 16 (masked lanes: only bytes below lim are written; a smaller block
+// keeps that rarely used variant's registers low).
+template <bool MASKED>
+struct Block {
+    static constexpr uint32_t kSyms = MASKED ? 16 : 128;
+    static constexpr uint32_t kWords = kSyms / 4;
+};
+
+template <bool MASKED>
+__device__ __forceinline__ void store_block(uint8_t *dst, uint32_t base, uint32_t lim,
+                                            const uint32_t (&o)[Block<MASKED>::kWords]) {
+    if (!MASKED || base + Block<MASKED>::kSyms <= lim) {
+        uint4 *d = reinterpret_cast<uint4 *>(dst + base);
+#pragma unroll
+        for (uint32_t k = 0; k < Block<MASKED>::kWords / 4; ++k)
+            d[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+    } else {
+#pragma unroll
+        for (uint32_t q = 0; q < Block<MASKED>::kWords; ++q)
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k)
+                if (base + 4 * q + k < lim) dst[base + 4 * q + k] = (uint8_t)(o[q] >> (8 * k));
+    }
+}
+
+// Symbols [s_begin, s_end) of one sub-stream (multiples of 64).
 template <int MODE, bool MASKED, bool CHECK, class Src>
 __device__ __forceinline__ uint32_t decode_part(const Src &src, uint32_t pos, uint32_t lim, const Tables &t,
-                                                uint8_t *dst, uint32_t &bad, uint32_t g_begin, uint32_t g_end) {
+                                                uint8_t *dst, uint32_t &bad, uint32_t s_begin, uint32_t s_end) {
+    constexpr uint32_t B = Block<MASKED>::kSyms;
 #pragma unroll 1
-    for (uint32_t g16 = g_begin; g16 < g_end; ++g16) {
-        uint32_t o[4];
+    for (uint32_t base = s_begin; base < s_end; base += B) {
+        uint32_t o[B / 4];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (uint32_t q = 0; q < B / 8; ++q) {
             uint32_t w[4];
             src.fetch4(pos >> 5, w);
             const uint32_t sh = pos & 31;
             const uint32_t h = (uint32_t)(((((uint64_t)w[0] << 32) | w[1]) << sh) >> 32);
             const uint32_t m = (uint32_t)(((((uint64_t)w[1] << 32) | w[2]) << sh) >> 32);
             const uint32_t l = (uint32_t)(((((uint64_t)w[2] << 32) | w[3]) << sh) >> 32);
-            decode8<MODE, MASKED, CHECK>(h, m, l, pos, bad, t, g16 * 16 + q * 8, lim, o[2 * q], o[2 * q + 1]);
+            decode8<MODE, MASKED, CHECK>(h, m, l, pos, bad, t, base + q * 8, lim, o[2 * q], o[2 * q + 1]);
         }
-        if (!MASKED) {
-            *reinterpret_cast<uint4 *>(dst + g16 * 16) = make_uint4(o[0], o[1], o[2], o[3]);
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (g16 * 16 + q * 4 + k < lim) dst[g16 * 16 + q * 4 + k] = (uint8_t)(o[q] >> (8 * k));
-        }
+        store_block<MASKED>(dst, base, lim, o);
     }
     return pos;
 }
@@ -217,6 +242,16 @@ __device__ __forceinline__ SpanEntries load_span(uint64_t grp, uint64_t num_sub,
     e.w_next = e.has_next ? cwo[g1 / spc] : cwo[num_chunks];
     e.off_next = e.has_next ? sub_off[g1] : 0u;
     return e;
+}
+
+// Per-lane form (each lane may hold a different group's entries).
+__device__ __forceinline__ void span_words_lane(const SpanEntries &e, uint64_t payload_words, uint64_t &lo,
+                                                uint64_t &hi) {
+    lo = (e.w_first * 32 + e.off_first) >> 5;
+    hi = (e.w_next * 32 + e.off_next + 31) >> 5;
+    if (lo > payload_words) lo = payload_words;
+    if (hi > payload_words) hi = payload_words;
+    if (hi < lo) hi = lo;
 }
 
 __device__ __forceinline__ void span_words(const SpanEntries &e, uint64_t payload_words, uint64_t &lo, uint64_t &hi) {
@@ -391,11 +426,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
             variant = allfull ? (complete ? 0 : 1) : 2;
             pos = job.pos0;
             if (variant == 0)
-                pos = decode_part<MODE, false, false>(src, pos, job.lim, t, dst, bad, 0, kSub / 32);
+                pos = decode_part<MODE, false, false>(src, pos, job.lim, t, dst, bad, 0, kSub / 2);
             else if (variant == 1)
-                pos = decode_part<MODE, false, true>(src, pos, job.lim, t, dst, bad, 0, kSub / 32);
+                pos = decode_part<MODE, false, true>(src, pos, job.lim, t, dst, bad, 0, kSub / 2);
             else
-                pos = decode_part<MODE, true, true>(src, pos, job.lim, t, dst, bad, 0, kSub / 32);
+                pos = decode_part<MODE, true, true>(src, pos, job.lim, t, dst, bad, 0, kSub / 2);
         }
         if (more) {
             span_words(nspan, payload_words, nlo, nhi);
@@ -403,11 +438,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
         }
         if (staged) {
             if (variant == 0)
-                pos = decode_part<MODE, false, false>(src, pos, job.lim, t, dst, bad, kSub / 32, kSub / 16);
+                pos = decode_part<MODE, false, false>(src, pos, job.lim, t, dst, bad, kSub / 2, kSub);
             else if (variant == 1)
-                pos = decode_part<MODE, false, true>(src, pos, job.lim, t, dst, bad, kSub / 32, kSub / 16);
+                pos = decode_part<MODE, false, true>(src, pos, job.lim, t, dst, bad, kSub / 2, kSub);
             else
-                pos = decode_part<MODE, true, true>(src, pos, job.lim, t, dst, bad, kSub / 32, kSub / 16);
+                pos = decode_part<MODE, true, true>(src, pos, job.lim, t, dst, bad, kSub / 2, kSub);
             if (job.ok && (bad || pos != job.pos_want)) flag_corrupt(status);
         }
 
@@ -421,7 +456,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 
 // Groups whose span exceeds the LDS budget, decoded from global memory (the
 // same span test as the main kernel picks them; each lane reads its words
-// directly).  Grid-stride over all groups.
+// directly).  The first wave of a workgroup tests 64 groups at once (one per
+// lane), then the workgroup decodes the ones that were not staged, so that
+// a stream with no such group costs one round of entry loads.
+constexpr uint32_t kTestBatch = 64;
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
@@ -430,6 +469,8 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status, uint32_t stage_cap) {
     __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 16];
     __shared__ uint32_t area_tab[8];
+    __shared__ uint32_t todo[kTestBatch];
+    __shared__ uint32_t ntodo;
     const uint32_t tid = threadIdx.x;
     const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
     const pc_codebook *cbp = reinterpret_cast<const pc_codebook *>(cb);
@@ -439,24 +480,38 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     t.lut = reinterpret_cast<const uint16_t *>(tab4);
     t.sym = reinterpret_cast<const uint8_t *>(tab4);
     t.area = area_tab;
-    for (uint64_t grp = blockIdx.x; grp < num_groups; grp += gridDim.x) {
-        uint64_t lo, hi;
-        span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
-        if (span_staged(lo, hi, payload_words, stage_cap)) continue;  // done by the main kernel
-        if (!loaded) {
+    for (uint64_t base = (uint64_t)blockIdx.x * kTestBatch; base < num_groups;
+         base += (uint64_t)gridDim.x * kTestBatch) {
+        if (tid == 0) ntodo = 0;
+        __syncthreads();
+        if (tid < kTestBatch && base + tid < num_groups) {
+            uint64_t lo, hi;
+            span_words_lane(load_span(base + tid, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
+            if (!span_staged(lo, hi, payload_words, stage_cap)) todo[atomicAdd(&ntodo, 1u)] = tid;
+        }
+        __syncthreads();
+        const uint32_t nt = ntodo;
+        if (nt && !loaded) {
             load_tables<MODE>(cbb, tab4, area_tab, tid);
             __syncthreads();
             loaded = true;
         }
-        const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
-        const LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
-        const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
-        if (payload_words <= wbase) continue;  // nothing readable: every lane was flagged
-        uint8_t *dst = out + (grp * kThreads + tid) * kSub;
-        GlobalWords src{payload + wbase, payload_words - wbase - 1};
-        uint32_t bad = 0;
-        const uint32_t pos_end = decode_part<MODE, true, true>(src, job.pos0, job.lim, t, dst, bad, 0, kSub / 16);
-        if (job.ok && (bad || pos_end != job.pos_want)) flag_corrupt(status);
+        for (uint32_t i = 0; i < nt; ++i) {
+            const uint64_t grp = base + todo[i];
+            uint64_t lo, hi;
+            span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
+            const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
+            const LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
+            const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
+            if (payload_words <= wbase) continue;  // nothing readable: every lane was flagged
+            uint8_t *dst = out + (grp * kThreads + tid) * kSub;
+            GlobalWords src{payload + wbase, payload_words - wbase - 1};
+            uint32_t bad = 0;
+            const uint32_t pos_end =
+                decode_part<MODE, true, true>(src, job.pos0, job.lim, t, dst, bad, 0, kSub);
+            if (job.ok && (bad || pos_end != job.pos_want)) flag_corrupt(status);
+        }
+        __syncthreads();  // todo and ntodo are rewritten by the next batch
     }
 }
 
@@ -494,12 +549,14 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     }
     uint64_t grid = (uint64_t)num_cus * kGroupsPerCU;
     if (grid > num_groups) grid = num_groups;
+    uint64_t grid_g = (uint64_t)num_cus * kGroupsPerCU;
+    if (grid_g > (num_groups + kTestBatch - 1) / kTestBatch) grid_g = (num_groups + kTestBatch - 1) / kTestBatch;
     if (num_sub >= 0xFFFFFFFFull) return hipErrorInvalidValue;
 #define PC_DEC(K)                                                                                             \
     hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), shmem, stream, cb, payload, payload_words,     \
                        chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, nc, out, status, (uint32_t)cap)
 #define PC_DEC_G(K)                                                                                           \
-    hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), 0, stream, cb, payload, payload_words,         \
+    hipLaunchKernelGGL(K, dim3((uint32_t)grid_g), dim3(kThreads), 0, stream, cb, payload, payload_words,       \
                        chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, nc, out, status, (uint32_t)cap)
     if (mode == kDecodeLut12) {
         PC_DEC(decode_kernel<kDecodeLut12>);
