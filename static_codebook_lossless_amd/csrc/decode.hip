@@ -130,62 +130,90 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
     asm volatile("" : "+v"(o0), "+v"(o1));
 }
 
-// Decoded bytes leave a lane in blocks of 64 (full lanes: four adjacent
-// 16-byte stores to one 64-byte segment, so the L2 receives whole segments
-// instead of 16-byte pieces of lines that other stores complete much later)
-// or of 16 (masked lanes: only bytes below lim are written; a smaller block
-// keeps that rarely used variant's registers low).
-template <bool MASKED>
-struct Block {
-    static constexpr uint32_t kSyms = MASKED ? 16 : 128;
-    static constexpr uint32_t kWords = kSyms / 4;
-};
-
-template <bool MASKED>
-__device__ __forceinline__ void store_block(uint8_t *dst, uint32_t base, uint32_t lim,
-                                            const uint32_t (&o)[Block<MASKED>::kWords]) {
-    if (!MASKED || base + Block<MASKED>::kSyms <= lim) {
-        uint4 *d = reinterpret_cast<uint4 *>(dst + base);
-#pragma unroll
-        for (uint32_t k = 0; k < Block<MASKED>::kWords / 4; ++k)
-            d[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
-    } else {
-#pragma unroll
-        for (uint32_t q = 0; q < Block<MASKED>::kWords; ++q)
-#pragma unroll
-            for (uint32_t k = 0; k < 4; ++k)
-                if (base + 4 * q + k < lim) dst[base + 4 * q + k] = (uint8_t)(o[q] >> (8 * k));
-    }
-}
-
-// Symbols [s_begin, s_end) of one sub-stream (multiples of 64).
-template <int MODE, bool MASKED, bool CHECK, class Src>
-__device__ __forceinline__ uint32_t decode_part(const Src &src, uint32_t pos, uint32_t lim, const Tables &t,
-                                                uint8_t *dst, uint32_t &bad, uint32_t s_begin, uint32_t s_end) {
-    constexpr uint32_t B = Block<MASKED>::kSyms;
+// Masked decode (the second kernel): symbols [s_begin, s_end) of one
+// sub-stream in blocks of 16; a lane writes only its bytes below lim (lanes
+// past the end of the stream own none).
+template <int MODE, class Src>
+__device__ __forceinline__ uint32_t decode_masked(const Src &src, uint32_t pos, uint32_t lim, const Tables &t,
+                                                  uint8_t *dst, uint32_t &bad, uint32_t s_begin, uint32_t s_end) {
 #pragma unroll 1
-    for (uint32_t base = s_begin; base < s_end; base += B) {
-        uint32_t o[B / 4];
+    for (uint32_t base = s_begin; base < s_end; base += 16) {
+        uint32_t o[4];
 #pragma unroll
-        for (uint32_t q = 0; q < B / 8; ++q) {
+        for (uint32_t q = 0; q < 2; ++q) {
             uint32_t w[4];
             src.fetch4(pos >> 5, w);
             const uint32_t sh = pos & 31;
             const uint32_t h = (uint32_t)(((((uint64_t)w[0] << 32) | w[1]) << sh) >> 32);
             const uint32_t m = (uint32_t)(((((uint64_t)w[1] << 32) | w[2]) << sh) >> 32);
             const uint32_t l = (uint32_t)(((((uint64_t)w[2] << 32) | w[3]) << sh) >> 32);
-            decode8<MODE, MASKED, CHECK>(h, m, l, pos, bad, t, base + q * 8, lim, o[2 * q], o[2 * q + 1]);
+            decode8<MODE, true, true>(h, m, l, pos, bad, t, base + q * 8, lim, o[2 * q], o[2 * q + 1]);
         }
-        store_block<MASKED>(dst, base, lim, o);
+        if (base + 16 <= lim) {
+            *reinterpret_cast<uint4 *>(dst + base) = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q)
+#pragma unroll
+                for (uint32_t k = 0; k < 4; ++k)
+                    if (base + 4 * q + k < lim) dst[base + 4 * q + k] = (uint8_t)(o[q] >> (8 * k));
+        }
     }
     return pos;
+}
+
+// Loaded values pass through pin() where they are first needed: the empty
+// asm fixes that point, so the compiler cannot hoist arithmetic on a value
+// still in flight (and with it a wait for every load issued before it) to
+// right after the load.  The loads themselves are unconditional, with
+// clamped indices, for the same reason: a conditional load merged with a
+// default value needs its result at the merge.
+__device__ __forceinline__ void pin(uint32_t &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(uint64_t &v) { asm volatile("" : "+v"(v)); }
+
+__device__ __forceinline__ uint32_t vgpr_copy(uint32_t v) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// Half a sub-stream (128 symbols) of a lane whose 256 symbols all lie in
+// [0, n), decoded into registers and then stored as one 128-byte line per
+// lane (eight adjacent 16-byte stores: the L2 receives whole lines, not
+// 16-byte pieces that other stores complete much later).
+constexpr uint32_t kHalf = kSub / 2;
+constexpr uint32_t kHalfWords = kHalf / 4;
+
+template <int MODE, bool CHECK>
+__device__ __forceinline__ uint32_t decode_half(const LdsWords &src, uint32_t pos, const Tables &t, uint32_t &bad,
+                                                uint32_t (&o)[kHalfWords]) {
+#pragma unroll
+    for (uint32_t q = 0; q < kHalf / 8; ++q) {
+        uint32_t w[4];
+        src.fetch4(pos >> 5, w);
+        const uint32_t sh = pos & 31;
+        const uint32_t h = (uint32_t)(((((uint64_t)w[0] << 32) | w[1]) << sh) >> 32);
+        const uint32_t m = (uint32_t)(((((uint64_t)w[1] << 32) | w[2]) << sh) >> 32);
+        const uint32_t l = (uint32_t)(((((uint64_t)w[2] << 32) | w[3]) << sh) >> 32);
+        decode8<MODE, false, CHECK>(h, m, l, pos, bad, t, 0, kHalf, o[2 * q], o[2 * q + 1]);
+    }
+    return pos;
+}
+
+__device__ __forceinline__ void store_half(uint8_t *dst, const uint32_t (&o)[kHalfWords]) {
+    uint4 *d = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (uint32_t k = 0; k < kHalfWords / 4; ++k)
+        d[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
 }
 
 // Container entries a lane depends on (loaded one group ahead).
 struct LaneMeta {
     uint64_t w0, w1;      // chunk_word_offset[c], [c + 1]
     uint32_t cbits;       // chunk_bits[c]
-    uint32_t start, end;  // sub-stream start; next start (all ones: chunk_bits)
+    uint32_t start;       // sub-stream start
+    uint32_t next;        // next sub-stream's start (meaningful if has_end)
+    uint32_t has_end;     // 0: the sub-stream ends at chunk_bits
     uint32_t lim;         // symbols owed by this lane (0 if inactive)
     uint32_t first;       // first sub-stream of its chunk
 };
@@ -193,23 +221,24 @@ struct LaneMeta {
 __device__ __forceinline__ LaneMeta load_meta(uint64_t g, uint64_t num_sub, uint64_t n, uint32_t chunk,
                                               const uint32_t *chunk_bits, const uint64_t *cwo,
                                               const uint32_t *sub_off) {
-    LaneMeta m{0, 0, 0, 0, 0, 0, 0};
-    if (g < num_sub) {
-        const uint32_t spc = chunk / kSub;
-        const uint64_t c = (uint32_t)g / spc;  // num_sub < 2^32 (checked by the launcher)
-        const uint32_t j = (uint32_t)(g - c * spc);
-        const uint64_t cbase = c * chunk;
-        const uint32_t lenc = (uint32_t)((n - cbase) < chunk ? (n - cbase) : chunk);
-        const uint32_t nsub_c = (lenc + kSub - 1) / kSub;
-        const uint32_t left = lenc - j * kSub;
-        m.lim = left < kSub ? left : kSub;
-        m.first = j == 0;
-        m.w0 = cwo[c];
-        m.w1 = cwo[c + 1];
-        m.cbits = chunk_bits[c];
-        m.start = sub_off[g];
-        m.end = (j + 1 < nsub_c) ? sub_off[g + 1] : 0xFFFFFFFFu;
-    }
+    const bool active = g < num_sub;
+    const uint32_t gc = (uint32_t)(active ? g : num_sub - 1);  // num_sub < 2^32 (checked by the launcher)
+    const uint32_t spc = chunk / kSub;
+    const uint32_t c = gc / spc;
+    const uint32_t j = gc - c * spc;
+    const uint64_t cbase = (uint64_t)c * chunk;
+    const uint32_t lenc = (uint32_t)((n - cbase) < chunk ? (n - cbase) : chunk);
+    const uint32_t nsub_c = (lenc + kSub - 1) / kSub;
+    const uint32_t left = lenc - j * kSub;
+    LaneMeta m;
+    m.lim = active ? (left < kSub ? left : kSub) : 0;
+    m.first = j == 0;
+    m.has_end = j + 1 < nsub_c;
+    m.w0 = cwo[c];
+    m.w1 = cwo[c + 1];
+    m.cbits = chunk_bits[c];
+    m.start = sub_off[gc];
+    m.next = sub_off[vgpr_copy(m.has_end ? gc + 1 : gc)];
     return m;
 }
 
@@ -220,15 +249,9 @@ __device__ __forceinline__ LaneMeta load_meta(uint64_t g, uint64_t num_sub, uint
 // every lane later checks its own range against the span.
 struct SpanEntries {
     uint64_t w_first, w_next;
-    uint32_t off_first, off_next;
+    uint32_t off_first, off_next;  // off_next: meaningful if has_next
     uint32_t has_next;
 };
-
-__device__ __forceinline__ uint32_t vgpr_copy(uint32_t v) {
-    uint32_t r;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
-    return r;
-}
 
 __device__ __forceinline__ SpanEntries load_span(uint64_t grp, uint64_t num_sub, uint32_t chunk, uint64_t num_chunks,
                                                  const uint64_t *cwo, const uint32_t *sub_off) {
@@ -239,24 +262,38 @@ __device__ __forceinline__ SpanEntries load_span(uint64_t grp, uint64_t num_sub,
     e.has_next = g1 < num_sub;
     e.w_first = cwo[g0 / spc];
     e.off_first = sub_off[g0];
-    e.w_next = e.has_next ? cwo[g1 / spc] : cwo[num_chunks];
-    e.off_next = e.has_next ? sub_off[g1] : 0u;
+    // opaque indices: a load the compiler could merge with the one above
+    // would come back as a conditional load plus a copy that waits for it
+    e.w_next = cwo[vgpr_copy(e.has_next ? g1 / spc : (uint32_t)num_chunks)];
+    e.off_next = sub_off[vgpr_copy(e.has_next ? g1 : g0)];
     return e;
+}
+
+// Bit addresses of the span's ends (the first use of the loaded entries).
+__device__ __forceinline__ void span_bits(SpanEntries e, uint64_t &a, uint64_t &b) {
+    pin(e.w_first);
+    pin(e.w_next);
+    pin(e.off_first);
+    pin(e.off_next);
+    a = e.w_first * 32 + e.off_first;
+    b = e.w_next * 32 + (e.has_next ? e.off_next : 0u);
 }
 
 // Per-lane form (each lane may hold a different group's entries).
 __device__ __forceinline__ void span_words_lane(const SpanEntries &e, uint64_t payload_words, uint64_t &lo,
                                                 uint64_t &hi) {
-    lo = (e.w_first * 32 + e.off_first) >> 5;
-    hi = (e.w_next * 32 + e.off_next + 31) >> 5;
+    uint64_t a, b;
+    span_bits(e, a, b);
+    lo = a >> 5;
+    hi = (b + 31) >> 5;
     if (lo > payload_words) lo = payload_words;
     if (hi > payload_words) hi = payload_words;
     if (hi < lo) hi = lo;
 }
 
 __device__ __forceinline__ void span_words(const SpanEntries &e, uint64_t payload_words, uint64_t &lo, uint64_t &hi) {
-    const uint64_t a = e.w_first * 32 + e.off_first;
-    const uint64_t b = e.w_next * 32 + e.off_next;
+    uint64_t a, b;
+    span_bits(e, a, b);
     lo = uniform64(a >> 5);
     hi = uniform64((b + 31) >> 5);
     if (lo > payload_words) lo = payload_words;
@@ -265,32 +302,27 @@ __device__ __forceinline__ void span_words(const SpanEntries &e, uint64_t payloa
 }
 
 // Prefetch of a staged span into registers: one 16-byte load per quad of
-// words, unconditional and branch-free (an index past the last whole quad is
-// clamped; such quads are never staged), plus the up to 3 words after the
-// last whole quad as single-word loads.  Nothing is read at or past
+// words, unconditional and branch-free (control flow here would make the
+// compiler's wait counting conservative for the whole loop).  Quad indices
+// are clamped to the payload's last whole quad (the kernel runs only when
+// there is one); quads past it, or of a span too large to stage, are never
+// staged.  The up to 3 words after the last whole quad are read while
+// staging, by the one lane that needs them.  Nothing is read at or past
 // payload_words.
 struct Prefetch {
     uint4 q[kPrefetch];
-    uint32_t tail[3];
 };
 
 __device__ __forceinline__ void issue_prefetch(Prefetch &pf, const uint32_t *payload, uint64_t payload_words,
-                                               uint64_t lo, uint64_t hi, uint32_t stage_cap, uint32_t tid) {
-    const uint64_t wb = lo & ~(uint64_t)(kRow - 1);
-    if (hi - wb > stage_cap || payload_words <= wb) return;
-    const uint64_t full_q = (payload_words - wb) / 4;
-    const uint4 *src = reinterpret_cast<const uint4 *>(payload + wb);
-    if (full_q > 0) {
+                                               uint64_t lo, bool live, uint32_t tid) {
+    const uint64_t q0 = (lo & ~(uint64_t)(kRow - 1)) / 4;
+    const uint64_t last_q = payload_words / 4 - 1;
+    const uint4 *src = reinterpret_cast<const uint4 *>(payload);
 #pragma unroll
-        for (uint32_t k = 0; k < kPrefetch; ++k) {
-            const uint64_t q = tid + k * kThreads;
-            pf.q[k] = load_stream16(src + (q < full_q ? q : full_q - 1));
-        }
-    }
-#pragma unroll
-    for (uint32_t t = 0; t < 3; ++t) {
-        const uint64_t i = wb + 4 * full_q + t;
-        pf.tail[t] = payload[i < payload_words ? i : payload_words - 1];
+    for (uint32_t k = 0; k < kPrefetch; ++k) {
+        uint64_t q = q0 + tid + k * kThreads;
+        q = live ? (q < last_q ? q : last_q) : 0;  // not live: one line, read by every lane
+        pf.q[k] = load_stream16(src + q);
     }
 }
 
@@ -327,9 +359,14 @@ struct LaneJob {
     uint32_t lim, pos0, pos_want;
 };
 
-__device__ __forceinline__ LaneJob lane_job(const LaneMeta &m, bool kind_ok, uint64_t payload_words, uint64_t wbase,
+__device__ __forceinline__ LaneJob lane_job(LaneMeta m, bool kind_ok, uint64_t payload_words, uint64_t wbase,
                                             uint64_t hi, uint32_t *status) {
-    const uint32_t end = m.end == 0xFFFFFFFFu ? m.cbits : m.end;
+    pin(m.w0);
+    pin(m.w1);
+    pin(m.cbits);
+    pin(m.start);
+    pin(m.next);
+    const uint32_t end = m.has_end ? m.next : m.cbits;
     const uint64_t abs_s = m.w0 * 32 + m.start, abs_e = m.w0 * 32 + end;
     const bool active = m.lim > 0;
     LaneJob j;
@@ -343,11 +380,17 @@ __device__ __forceinline__ LaneJob lane_job(const LaneMeta &m, bool kind_ok, uin
     return j;
 }
 
+// Main kernel: the full groups (all 256 sub-streams of 256 symbols inside
+// [0, n)) whose span fits the staging rows, so no lane needs masking.  Each
+// half's 128 bytes per lane are stored as soon as they are decoded.  Lanes
+// of a corrupt sub-stream decode from the start of the staged span (LDS
+// reads are clamped) and write unspecified bytes into their own 256-byte
+// range.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
     const uint32_t *__restrict__ chunk_bits, const uint64_t *__restrict__ cwo,
-    const uint32_t *__restrict__ sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub, uint64_t num_groups,
+    const uint32_t *__restrict__ sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub, uint64_t num_full,
     uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status, uint32_t stage_cap) {
     // Tables at fixed LDS addresses (folded into the instructions' offset
     // fields); the payload staging rows are the dynamic part.
@@ -368,12 +411,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 
     // ---- prologue: loads of the first group --------------------------
     uint64_t grp = blockIdx.x;
-    if (grp >= num_groups) return;
+    if (grp >= num_full) return;
     LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
     uint64_t lo, hi;
     span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
     Prefetch pf;
-    issue_prefetch(pf, payload, payload_words, lo, hi, stage_cap, tid);
+    issue_prefetch(pf, payload, payload_words, lo, true, tid);
+    uint32_t o1[kHalfWords], o2[kHalfWords];
 
     for (;;) {
         const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
@@ -381,6 +425,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
         const bool staged = span_staged(lo, hi, payload_words, stage_cap);
         // ---- stage the current group (its loads were issued earlier) --
         __syncthreads();  // every lane is done with the previous group's rows
+        // wait for the whole prefetch here, on every path (waits left to the
+        // compiler would sit in the branches below, and every later write
+        // of these registers would wait again, for whatever is in flight)
+#pragma unroll
+        for (uint32_t k = 0; k < kPrefetch; ++k) {
+            pin(pf.q[k].x);
+            pin(pf.q[k].y);
+            pin(pf.q[k].z);
+            pin(pf.q[k].w);
+        }
         if (staged) {
             const uint32_t nq = (uint32_t)((cnt + 3) / 4);
             const uint64_t full_q = (payload_words - wbase) / 4;
@@ -390,10 +444,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
                 if (q < nq && q <= full_q) {
                     uint32_t v[4] = {pf.q[k].x, pf.q[k].y, pf.q[k].z, pf.q[k].w};
                     if (q == full_q) {  // the words after the last whole quad
-                        v[0] = pf.tail[0];
-                        v[1] = pf.tail[1];
-                        v[2] = pf.tail[2];
-                        v[3] = 0;
+#pragma unroll
+                        for (uint32_t w = 0; w < 4; ++w) {
+                            const uint64_t i = wbase + 4 * full_q + w;
+                            v[w] = i < payload_words ? payload[i] : 0u;
+                        }
                     }
                     const uint32_t i = row_index(4 * q);  // a multiple of 4
                     const uint4 qv = make_uint4(v[0], v[1], v[2], v[3]);
@@ -405,45 +460,39 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
         __syncthreads();
 
         // ---- the next group's entries (its payload: halfway through) ----
+        // Loads and prefetch are issued on every pass (for the last, of this
+        // group's entries and of one payload line): control flow around
+        // them makes the compiler's wait counting conservative, and it then
+        // waits for the prefetch right after issuing it.
         const uint64_t nxt = grp + gridDim.x;
-        const bool more = nxt < num_groups;
-        LaneMeta nmeta{0, 0, 0, 0, 0, 0, 0};
-        SpanEntries nspan{0, 0, 0, 0, 0};
-        if (more) {
-            nmeta = load_meta(nxt * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
-            nspan = load_span(nxt, num_sub, chunk, num_chunks, cwo, sub_off);
-        }
+        const bool more = nxt < num_full;
+        const uint64_t nxt_c = more ? nxt : grp;
+        const LaneMeta nmeta = load_meta(nxt_c * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
+        const SpanEntries nspan = load_span(nxt_c, num_sub, chunk, num_chunks, cwo, sub_off);
         // ---- decode: first half, the next group's payload loads, second half
         uint64_t nlo = 0, nhi = 0;
         LaneJob job{false, 0, 0, 0};
-        int variant = 0;  // 0: all lanes owe 256 symbols, complete code; 1: same, check codes; 2: masked
         uint8_t *dst = out + (grp * kThreads + tid) * kSub;
-        LdsWords src{stage, (uint32_t)(cnt > 0 ? cnt - 1 : 0)};
+        const LdsWords src{stage, (uint32_t)(cnt > 0 ? cnt - 1 : 0)};
         uint32_t bad = 0, pos = 0;
         if (staged) {
             job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
-            const bool allfull = __syncthreads_count(job.lim == kSub) == (int)kThreads;
-            variant = allfull ? (complete ? 0 : 1) : 2;
             pos = job.pos0;
-            if (variant == 0)
-                pos = decode_part<MODE, false, false>(src, pos, job.lim, t, dst, bad, 0, kSub / 2);
-            else if (variant == 1)
-                pos = decode_part<MODE, false, true>(src, pos, job.lim, t, dst, bad, 0, kSub / 2);
+            if (complete)
+                pos = decode_half<MODE, false>(src, pos, t, bad, o1);
             else
-                pos = decode_part<MODE, true, true>(src, pos, job.lim, t, dst, bad, 0, kSub / 2);
+                pos = decode_half<MODE, true>(src, pos, t, bad, o1);
+            store_half(dst, o1);
         }
-        if (more) {
-            span_words(nspan, payload_words, nlo, nhi);
-            issue_prefetch(pf, payload, payload_words, nlo, nhi, stage_cap, tid);
-        }
+        span_words(nspan, payload_words, nlo, nhi);
+        issue_prefetch(pf, payload, payload_words, nlo, more, tid);
         if (staged) {
-            if (variant == 0)
-                pos = decode_part<MODE, false, false>(src, pos, job.lim, t, dst, bad, kSub / 2, kSub);
-            else if (variant == 1)
-                pos = decode_part<MODE, false, true>(src, pos, job.lim, t, dst, bad, kSub / 2, kSub);
+            if (complete)
+                pos = decode_half<MODE, false>(src, pos, t, bad, o2);
             else
-                pos = decode_part<MODE, true, true>(src, pos, job.lim, t, dst, bad, kSub / 2, kSub);
+                pos = decode_half<MODE, true>(src, pos, t, bad, o2);
             if (job.ok && (bad || pos != job.pos_want)) flag_corrupt(status);
+            store_half(dst + kHalf, o2);
         }
 
         if (!more) break;
@@ -454,9 +503,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     }
 }
 
-// Groups whose span exceeds the LDS budget, decoded from global memory (the
-// same span test as the main kernel picks them; each lane reads its words
-// directly).  The first wave of a workgroup tests 64 groups at once (one per
+// The groups the main kernel leaves: those whose span exceeds the LDS
+// budget (the same span test picks them) and the last group when it is not
+// full.  Each lane reads its words straight from global memory and writes
+// only bytes below its symbol count.  The first wave of a workgroup tests 64 groups at once (one per
 // lane), then the workgroup decodes the ones that were not staged, so that
 // a stream with no such group costs one round of entry loads.
 constexpr uint32_t kTestBatch = 64;
@@ -466,7 +516,8 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
     const uint32_t *__restrict__ chunk_bits, const uint64_t *__restrict__ cwo,
     const uint32_t *__restrict__ sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub, uint64_t num_groups,
-    uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status, uint32_t stage_cap) {
+    uint64_t num_full, uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status,
+    uint32_t stage_cap) {
     __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 16];
     __shared__ uint32_t area_tab[8];
     __shared__ uint32_t todo[kTestBatch];
@@ -487,7 +538,8 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
         if (tid < kTestBatch && base + tid < num_groups) {
             uint64_t lo, hi;
             span_words_lane(load_span(base + tid, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
-            if (!span_staged(lo, hi, payload_words, stage_cap)) todo[atomicAdd(&ntodo, 1u)] = tid;
+            if (base + tid >= num_full || !span_staged(lo, hi, payload_words, stage_cap))
+                todo[atomicAdd(&ntodo, 1u)] = tid;
         }
         __syncthreads();
         const uint32_t nt = ntodo;
@@ -508,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
             GlobalWords src{payload + wbase, payload_words - wbase - 1};
             uint32_t bad = 0;
             const uint32_t pos_end =
-                decode_part<MODE, true, true>(src, job.pos0, job.lim, t, dst, bad, 0, kSub);
+                decode_masked<MODE>(src, job.pos0, job.lim, t, dst, bad, 0, kSub);
             if (job.ok && (bad || pos_end != job.pos_want)) flag_corrupt(status);
         }
         __syncthreads();  // todo and ntodo are rewritten by the next batch
@@ -547,22 +599,26 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
         if (e != hipSuccess) return e;
         attr_set[mode] = true;
     }
+    // groups whose 256 sub-streams all hold 256 symbols inside [0, n)
+    // (the main kernel's prefetch needs one whole 16-byte quad of payload)
+    const uint64_t num_full = payload_words >= 4 ? n / ((uint64_t)kThreads * kSub) : 0;
     uint64_t grid = (uint64_t)num_cus * kGroupsPerCU;
-    if (grid > num_groups) grid = num_groups;
+    if (grid > num_full) grid = num_full;
     uint64_t grid_g = (uint64_t)num_cus * kGroupsPerCU;
     if (grid_g > (num_groups + kTestBatch - 1) / kTestBatch) grid_g = (num_groups + kTestBatch - 1) / kTestBatch;
     if (num_sub >= 0xFFFFFFFFull) return hipErrorInvalidValue;
 #define PC_DEC(K)                                                                                             \
     hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), shmem, stream, cb, payload, payload_words,     \
-                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, nc, out, status, (uint32_t)cap)
+                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_full, nc, out, status, (uint32_t)cap)
 #define PC_DEC_G(K)                                                                                           \
     hipLaunchKernelGGL(K, dim3((uint32_t)grid_g), dim3(kThreads), 0, stream, cb, payload, payload_words,       \
-                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, nc, out, status, (uint32_t)cap)
+                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, num_full, nc, out, status,    \
+                       (uint32_t)cap)
     if (mode == kDecodeLut12) {
-        PC_DEC(decode_kernel<kDecodeLut12>);
+        if (grid) PC_DEC(decode_kernel<kDecodeLut12>);
         PC_DEC_G(decode_global_kernel<kDecodeLut12>);
     } else {
-        PC_DEC(decode_kernel<kDecodeQlc>);
+        if (grid) PC_DEC(decode_kernel<kDecodeQlc>);
         PC_DEC_G(decode_global_kernel<kDecodeQlc>);
     }
 #undef PC_DEC

@@ -168,6 +168,17 @@ def test_edge_sizes(chunk):
             roundtrip(dcb, obook, x_np, chunk, qlc_decoder=(kind == "qlc"))
 
 
+def test_group_boundaries():
+    """Sizes around whole groups of 256 sub-streams (65536 symbols): full
+    groups and a ragged last group take different decode kernels."""
+    for kind, bits in (("huffman", None), ("qlc", (1, 3, 3, 3, 3, 5, 6, 7))):
+        dcb, obook = make_book(random_counts(21), kind, bits)
+        for chunk in (4096, 65536):
+            for n in (65535, 65536, 65537, 2 * 65536 - 256, 2 * 65536 + 255, 2 * 65536 + 256, 3 * 65536):
+                say("group boundary:", kind, "chunk", chunk, "n", n)
+                roundtrip(dcb, obook, skewed(n, n), chunk, qlc_decoder=(kind == "qlc"))
+
+
 def test_many_chunks_lookback():
     """Tens of thousands of small chunks: stresses the cross-chunk scan."""
     dcb, obook = make_book(random_counts(3))
@@ -188,6 +199,12 @@ def test_degenerate_data(kind):
         "one_rare_symbol": np.full(100_000, int(np.argmax(lengths)), np.uint8),
         "uniform": np.tile(np.arange(256, dtype=np.uint8), 400),
         "unseen_symbols_only": np.arange(40, 256, dtype=np.uint8).repeat(300),
+        # whole groups of 65536 symbols: a compressible one (staged in LDS),
+        # two of 12-bit codewords (too large to stage), a ragged tail
+        "staged_and_unstaged_groups": np.concatenate([
+            np.tile(np.arange(40, dtype=np.uint8), 1639)[:65536],
+            np.tile(np.arange(40, 256, dtype=np.uint8), 607)[:131072],
+            np.arange(40, dtype=np.uint8).repeat(25)]),
     }
     for cname, x_np in cases.items():
         say("degenerate:", kind, cname)
@@ -252,6 +269,7 @@ def test_corruptions_detected(kind):
     cw[4] += 1
     cases.append(("cwo+1", modified(enc, chunk_word_offset=cw), None))
     cases.append(("short payload", enc, total - 1))
+    cases.append(("payload under one quad", enc, 3))
     for cname, e2, pw in cases:
         say("  case", cname)
         _, st = decode_guarded(dcb, e2, pw)
