@@ -41,15 +41,17 @@ __device__ __forceinline__ void st_desc(uint64_t *p, uint64_t v) {
 // Exclusive prefix (in words) of chunk c over all earlier chunks.  Called by
 // one whole wave.  Chunk c's workgroup got ticket c from an atomic counter,
 // so every earlier chunk's workgroup is already running and will publish.
-// Each round reads 256 predecessors (4 per lane, nearest first) in one trip
-// to L2, so the walk back to the nearest published inclusive prefix rarely
-// takes more than one round.
+// Each round reads 128 predecessors (2 per lane, nearest first) in one trip
+// to memory and polls, without pausing, until all have published; it then
+// sums counts up to the nearest inclusive prefix, or walks 128 chunks
+// further back.  (Descriptors written on other dies are read through the
+// fabric: more loads per poll made each trip slower, measured.)
 // The wait on predecessors is bounded: it always ends once they publish,
 // but should an ordering bug ever leave a predecessor silent, the wave gives
 // up after ~2^20 polls (about a second) and sets bit 32 of workspace word 0
 // instead of spinning forever.
 constexpr uint32_t kMaxPolls = 1u << 20;
-constexpr int kLookWin = 4;  // descriptors per lane per round
+constexpr int kLookWin = 2;  // descriptors per lane per round
 
 __device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_t lane) {
     if (c == 0) {
@@ -83,7 +85,6 @@ __device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_
                 if (lane == 0) atomicOr(reinterpret_cast<unsigned long long *>(desc - 1), 1ull << 32);
                 return 0;
             }
-            __builtin_amdgcn_s_sleep(1);
         }
         bool found = false;
 #pragma unroll
@@ -239,16 +240,18 @@ __device__ __forceinline__ void make_group(uint32_t e0, uint32_t e1, uint32_t e2
 }
 
 // OR one group (ng bits of g) into the buffer at bit p (bit 0 = MSB of
-// buf[0]); it spans at most 3 words.
+// buf[0]); it spans at most 3 words.  All three ORs are issued for every
+// lane (an OR with zero changes nothing): with the second and third made
+// conditional, exec-masked LDS atomics of this shape were seen to lose
+// updates on gfx950 (one wave's words of a tile came out with bits missing,
+// varying from run to run).
 __device__ __forceinline__ void place_group(uint64_t g, uint32_t ng, uint32_t p, uint32_t *buf) {
     const uint64_t a = g << (64 - ng);
     const uint32_t hi = (uint32_t)(a >> 32), lo = (uint32_t)a;
     const uint32_t o = p & 31, wi = p >> 5;
     atomicOr(&buf[wi], hi >> o);
-    const uint32_t w1 = __builtin_amdgcn_alignbit(hi, lo, o);
-    const uint32_t w2 = __builtin_amdgcn_alignbit(lo, 0u, o);
-    if (w1) atomicOr(&buf[wi + 1], w1);
-    if (w2) atomicOr(&buf[wi + 2], w2);
+    atomicOr(&buf[wi + 1], __builtin_amdgcn_alignbit(hi, lo, o));
+    atomicOr(&buf[wi + 2], __builtin_amdgcn_alignbit(lo, 0u, o));
 }
 
 template <class SH>
