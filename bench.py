@@ -195,6 +195,68 @@ def _cpu_model():
 # ---------------------------------------------------------------------------
 
 
+def time_calls(fn, reps):
+    """Mean milliseconds of fn() (device work, timed with events on the
+    current stream) over reps calls after two warmup calls."""
+    import torch
+
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def qlc_leg(pc, W, dev):
+    """The QLC codebook on the GELU tensor (64 MiB, 16 KiB chunks): encode,
+    the generic 12-bit-peek decoder and the QLC decoder, with the QLC and
+    Huffman-12 bits per symbol of the same tensor."""
+    import numpy as np
+    import torch
+
+    w = W.WORKLOADS["gelu_act"]
+    counts = torch.zeros(256, dtype=torch.int64, device=dev)
+    for s in w.prev_seeds:
+        pc.pc_histogram(torch.from_numpy(W.make(w.name, s)).to(dev), counts)
+    counts_np = counts.cpu().numpy().astype(np.uint64)
+    x = torch.from_numpy(W.make(w.name, 0)).to(dev)
+    n = w.n
+    book_q = pc.pc_codebook_build(counts_np, "qlc", w.qlc_bits)
+    book_h = pc.pc_codebook_build(counts_np, "huffman")
+    dq = book_q.to(dev)
+    outs = pc.alloc_encode_outputs(n, w.chunk, dev)
+    out = torch.empty(n, dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    enc_ms = time_calls(lambda: pc.pc_encode(dq, x, w.chunk, outs), 10)
+    enc = pc.pc_encode(dq, x, w.chunk, outs)
+    dec_ms = time_calls(lambda: pc.pc_decode(dq, enc, out=out, status=st), 10)
+    ok_lut = int(st.item()) == 0 and bool(torch.equal(out, x))
+    st.zero_()
+    qdec_ms = time_calls(lambda: pc.pc_decode_qlc(dq, enc, out=out, status=st), 10)
+    ok_qlc = int(st.item()) == 0 and bool(torch.equal(out, x))
+    xc = pc.pc_histogram(x).cpu().numpy().astype(np.float64)
+    lq = pc.codebook_fields(book_q)["length"].astype(np.float64)
+    lh = pc.codebook_fields(book_h)["length"].astype(np.float64)
+    ls = pc.codebook_fields(pc.pc_codebook_build(xc.astype(np.uint64), "huffman"))["length"].astype(np.float64)
+    p = xc[xc > 0] / n
+    H = float(-(p * np.log2(p)).sum())
+    bq, bh, bs = (float((xc * l).sum()) / n for l in (lq, lh, ls))
+    return {"n_bytes": n, "chunk": w.chunk, "qlc_bits": list(w.qlc_bits),
+            "encode_GBps": round(n / (enc_ms * 1e-3) / 1e9, 1),
+            "decode_lut12_GBps": round(n / (dec_ms * 1e-3) / 1e9, 1),
+            "decode_qlc_GBps": round(n / (qdec_ms * 1e-3) / 1e9, 1),
+            "round_trip_ok": bool(ok_lut and ok_qlc),
+            "bits_per_symbol": {"qlc": round(bq, 5), "huffman12_same_counts": round(bh, 5),
+                                "huffman12_own_counts": round(bs, 5), "entropy": round(H, 5),
+                                "qlc_compressibility": round(1 - bq / 8, 5),
+                                "huffman12_compressibility": round(1 - bh / 8, 5)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +268,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the QLC (GELU tensor) and histogram measurements")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -347,6 +411,12 @@ def main():
         cpu, parity = cpu_baseline_leg(x_np, counts_prev, w.kind, w.qlc_bits, chunk, host_streams,
                                        args.cpu_seconds, threads)
 
+    secondary = None
+    if not args.no_secondary:
+        hist_ms = time_calls(lambda: pc.pc_histogram(x), 10)
+        secondary = {"histogram_GBps": round(n / (hist_ms * 1e-3) / 1e9, 1)}
+        secondary["qlc_gelu_act"] = qlc_leg(pc, W, dev)
+
     res = {
         "metric": "encode+decode GB/s (uncompressed bytes per round trip), 1 MI355X",
         "value": round(n / (ms_per_step * 1e-3) / 1e9, 2),
@@ -381,6 +451,7 @@ def main():
         "round_trip_ok": bool(st == 0 and same),
         "cpu_baseline": cpu,
         "oracle_parity_sample": parity,
+        "secondary": secondary,
     }
     print(json.dumps(res), flush=True)
     return 0 if (st == 0 and same and (parity is None or all(v for k, v in parity.items() if k != "chunks"))) else 1
