@@ -207,7 +207,7 @@ __device__ __forceinline__ void flush_tile(SH &sh, uint32_t *dst, uint32_t tile_
 // ---------------------------------------------------------------------------
 // Whole-chunk kernel (chunks of exactly NT tiles of THREADS x 16 symbols).
 //
-// Every symbol is looked up once: the table entry is code | length << 16.
+// Every symbol is looked up once: the table entry is code << 16 | length.
 // Per tile, each lane turns its 16 symbols into 4 groups (<= 48 bits each),
 // the tile's bit offsets come from a wave scan plus a scan of the wave
 // totals, and the groups are ORed straight into an LDS buffer that holds the
@@ -220,23 +220,24 @@ __device__ __forceinline__ void flush_tile(SH &sh, uint32_t *dst, uint32_t tile_
 
 template <uint32_t THREADS, int NT, uint32_t BUFW>
 struct ChunkShared {
-    uint32_t tab[256];                    // code | length << 16
+    uint32_t tab[256];                    // code << 16 | length
     uint32_t wave_tot[NT][THREADS / 64];  // per tile, per wave: bits
     uint32_t misc[4];
     uint32_t buf[BUFW + 8];
 };
 
-// Four table entries -> one group: g holds ng bits (right-aligned) once the
-// bits above ng are ignored.  The length field of an entry, shifted along,
-// always lands above the group's valid bits.
+// Four table entries -> one group of ng (<= 48) bits, right-aligned in g.
+// An entry is code << 16 | length: the length sits in the bits a shift
+// instruction reads as its count, and the code in the upper half, which the
+// instructions can take as an operand directly, so no field is extracted on
+// its own.
 __device__ __forceinline__ void make_group(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3, uint64_t &g,
                                            uint32_t &ng) {
-    const uint32_t l0 = e0 >> 16, l1 = e1 >> 16, l2 = e2 >> 16, l3 = e3 >> 16;
-    const uint32_t p01 = (e0 << l1) | (e1 & 0xFFFu);
-    const uint32_t n23 = l2 + l3;
-    const uint32_t p23 = __builtin_amdgcn_ubfe((e2 << l3) | (e3 & 0xFFFu), 0, n23);
+    const uint32_t p01 = ((e0 >> 16) << (e1 & 31)) | (e1 >> 16);
+    const uint32_t p23 = ((e2 >> 16) << (e3 & 31)) | (e3 >> 16);
+    const uint32_t n23 = (e2 & 0xFF) + (e3 & 0xFF);
     g = ((uint64_t)p01 << n23) | p23;
-    ng = l0 + l1 + n23;
+    ng = (e0 & 0xFF) + (e1 & 0xFF) + n23;
 }
 
 // OR one group (ng bits of g) into the buffer at bit p (bit 0 = MSB of
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
     if (tid == 0) sh.misc[0] = atomicAdd(reinterpret_cast<uint32_t *>(ws), 1u);
     if (tid < 256) {
         const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
-        sh.tab[tid] = reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid] | ((uint32_t)cbb[kOffLength + tid] << 16);
+        sh.tab[tid] = ((uint32_t)reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid] << 16) | cbb[kOffLength + tid];
     }
     for (uint32_t i = tid; i < (BUFW + 8) / 4; i += THREADS) reinterpret_cast<uint4 *>(sh.buf)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
