@@ -8,10 +8,9 @@ nothing from the product.
 
 What the pages fix, and the readings taken where they are silent:
 
-* "Single-Stage Huffman Encoder for ML Compression" (abstract): the codebook
-  is fixed and derived from the average probability distribution of previous
-  data batches, so no frequency analysis, codebook generation or codebook
-  transmission happens at run time.  Averaging is read as *pooled counts*
+* "Single-Stage Huffman Encoder for ML Compression" (abstract): one codebook
+  is fixed beforehand from the averaged byte statistics of earlier batches,
+  so nothing is counted, built or sent alongside the data at run time.  Averaging is read as *pooled counts*
   (sum of per-batch counts; all batches have equal size, so this is
   proportional to the mean PMF).
 * Every one of the 256 byte values must stay codable even if it never
@@ -28,7 +27,7 @@ What the pages fix, and the readings taken where they are silent:
   plot sorted PMFs): rank 0 is the most frequent symbol; equal counts are
   ranked by lower byte value first.  The in-area index is plain binary,
   most significant bit first.
-* Shannon entropy (the "ideal Shannon compressibility" of the first page)
+* Shannon entropy (the bound the first page compares the fixed code with)
   is the order-0 empirical entropy of the tensor's own byte histogram.
 
 Parity pins for every function here live in ``tests/test_oracle_codebook.py``
@@ -51,8 +50,8 @@ QLC_AREAS = 8
 QLC_PREFIX_BITS = 3
 
 # ----------------------------------------------------------------------------
-# Statistics (first page: "average probability distribution of previous
-# data batches").
+# Statistics (first page, abstract: the codebook comes from the averaged
+# distribution of earlier batches).
 # ----------------------------------------------------------------------------
 
 
