@@ -9,8 +9,9 @@
 // workgroup); its payload is one contiguous span of words.  Workgroups are
 // persistent and walk the groups with a stride of the grid size.  While a
 // workgroup decodes group k out of LDS, the loads of group k+1 (its
-// container entries and its payload span, into registers) are in flight, so
-// HBM latency is hidden behind decoding.  Per group:
+// container entries, then its payload span into registers, two 16-byte
+// loads per lane after each of the steps 6-13 of the first 128 symbols) are
+// in flight, so HBM latency is hidden behind decoding.  Per group:
 //   1. the staged span sits in LDS in rows of 36 words: 32 payload words plus
 //      copies of the next row's first four, so any 4-word window read stays
 //      in one row, rows start 16-byte aligned, and lanes whose sub-streams
@@ -21,15 +22,15 @@
 //      16-bit table entry ((32 - length) | symbol << 8) at the top 12 window
 //      bits and advance the window with two funnel shifts (v_alignbit) whose
 //      shift count is the entry itself (the instruction reads 5 bits);
-//   3. every 64 decoded bytes of a lane go out as four adjacent 16-byte
-//      stores;
+//   3. every 128 decoded bytes of a lane go out as eight adjacent 16-byte
+//      stores (whole 128-byte lines);
 //   4. the sub-stream must end exactly at the next sub-stream's first bit (or
 //      at chunk_bits); any mismatch sets *status = PC_ERR_CORRUPT.
 // A group whose span does not fit the LDS budget is left to a second kernel
 // that decodes it straight from global memory (only data that barely
-// compresses produces such groups).  The QLC variant replaces the 12-bit table with the
-// page's own decoder: a 3-bit area number, that area's fixed-width index, and
-// the 256-entry rank -> symbol table.
+// compresses produces such groups).  The QLC variant replaces the 12-bit
+// table with the page's own decoder: a 3-bit area number, that area's
+// fixed-width index, and the 256-entry rank -> symbol table.
 #include "pc_internal.h"
 
 namespace pc {
@@ -125,9 +126,11 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
     pos += 256 - s0 - s1;
     o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
     o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
-    // pack here: left to the scheduler, the packing sinks towards the store
-    // and keeps all eight entries of every step alive until then
+    // pack and check here: left to the scheduler, the packing sinks towards
+    // the store and the checks towards the end of the stream, and both keep
+    // all eight entries of every step alive until then
     asm volatile("" : "+v"(o0), "+v"(o1));
+    if (CHECK) asm volatile("" : "+v"(bad));
 }
 
 // Masked decode (the second kernel): symbols [s_begin, s_end) of one
@@ -184,9 +187,13 @@ __device__ __forceinline__ uint32_t vgpr_copy(uint32_t v) {
 constexpr uint32_t kHalf = kSub / 2;
 constexpr uint32_t kHalfWords = kHalf / 4;
 
-template <int MODE, bool CHECK>
+// side(q) runs after step q (8 symbols) of the 16: the memory instructions
+// of a group are spread over its decode steps, where the wave mostly waits
+// for LDS results, instead of being issued in bursts that stall the waves
+// of a workgroup together behind the CU's memory pipeline.
+template <int MODE, bool CHECK, class Side>
 __device__ __forceinline__ uint32_t decode_half(const LdsWords &src, uint32_t pos, const Tables &t, uint32_t &bad,
-                                                uint32_t (&o)[kHalfWords]) {
+                                                uint32_t (&o)[kHalfWords], Side &&side) {
 #pragma unroll
     for (uint32_t q = 0; q < kHalf / 8; ++q) {
         uint32_t w[4];
@@ -196,6 +203,8 @@ __device__ __forceinline__ uint32_t decode_half(const LdsWords &src, uint32_t po
         const uint32_t m = (uint32_t)(((((uint64_t)w[1] << 32) | w[2]) << sh) >> 32);
         const uint32_t l = (uint32_t)(((((uint64_t)w[2] << 32) | w[3]) << sh) >> 32);
         decode8<MODE, false, CHECK>(h, m, l, pos, bad, t, 0, kHalf, o[2 * q], o[2 * q + 1]);
+        side(q);
+        asm volatile("" ::: "memory");  // the side work stays at this step
     }
     return pos;
 }
@@ -313,17 +322,40 @@ struct Prefetch {
     uint4 q[kPrefetch];
 };
 
-__device__ __forceinline__ void issue_prefetch(Prefetch &pf, const uint32_t *payload, uint64_t payload_words,
-                                               uint64_t lo, bool live, uint32_t tid) {
+// The payload as the prefetch sees it: a global pointer passed through an
+// empty asm, so that the compiler no longer knows that nothing writes the
+// words and keeps each load at the decode step it is issued at (loads of
+// memory known to be read-only are moved freely, and end up together).
+typedef const __attribute__((address_space(1))) u32x4 gquad;
+
+__device__ __forceinline__ gquad *opaque_quads(const uint32_t *payload) {
+    gquad *p = (gquad *)payload;
+    asm volatile("" : "+s"(p));
+    return p;
+}
+
+// Quad k of lane tid of the span [lo, hi): quads past the span's last one
+// (or the payload's last whole one) read that quad again, so lanes with no
+// quad of their own add no traffic.
+__device__ __forceinline__ uint64_t last_quad(uint64_t lo, uint64_t hi, uint64_t payload_words) {
     const uint64_t q0 = (lo & ~(uint64_t)(kRow - 1)) / 4;
-    const uint64_t last_q = payload_words / 4 - 1;
-    const uint4 *src = reinterpret_cast<const uint4 *>(payload);
+    uint64_t qe = (hi + 3) / 4;  // one past the span's last quad
+    if (qe <= q0) qe = q0 + 1;
+    if (qe > payload_words / 4) qe = payload_words / 4;
+    return qe - 1;
+}
+
+__device__ __forceinline__ void prefetch_quad(Prefetch &pf, uint32_t k, gquad *payload, uint64_t lo,
+                                              uint64_t q_last, uint32_t tid) {
+    const uint64_t q = (lo & ~(uint64_t)(kRow - 1)) / 4 + tid + k * kThreads;
+    const u32x4 v = __builtin_nontemporal_load(payload + (q < q_last ? q : q_last));
+    pf.q[k] = make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void issue_prefetch(Prefetch &pf, gquad *payload, uint64_t lo, uint64_t q_last,
+                                               uint32_t tid) {
 #pragma unroll
-    for (uint32_t k = 0; k < kPrefetch; ++k) {
-        uint64_t q = q0 + tid + k * kThreads;
-        q = live ? (q < last_q ? q : last_q) : 0;  // not live: one line, read by every lane
-        pf.q[k] = load_stream16(src + q);
-    }
+    for (uint32_t k = 0; k < kPrefetch; ++k) prefetch_quad(pf, k, payload, lo, q_last, tid);
 }
 
 // Tables into LDS (shared by both kernels).
@@ -380,6 +412,120 @@ __device__ __forceinline__ LaneJob lane_job(LaneMeta m, bool kind_ok, uint64_t p
     return j;
 }
 
+// The group loop of a workgroup (CHECK: test every table entry for "no
+// codeword", needed only when the code is incomplete).  Every lane decodes
+// on every pass; a group whose span is not staged decodes stale rows and
+// stores nothing (the second kernel decodes it).
+template <int MODE, bool CHECK>
+__device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const Tables &t, bool kind_ok,
+                                              uint32_t *stage, uint4 *stage4, const uint32_t *payload,
+                                              uint64_t payload_words, const uint32_t *chunk_bits,
+                                              const uint64_t *cwo, const uint32_t *sub_off, uint64_t n,
+                                              uint32_t chunk, uint64_t num_sub, uint64_t num_full,
+                                              uint64_t num_chunks, uint8_t *out, uint32_t *status,
+                                              uint32_t stage_cap) {
+    gquad *pq = opaque_quads(payload);
+    // ---- prologue: loads of the first group --------------------------
+    LaneMeta meta = load_meta(grp * kThreads + tid0, num_sub, n, chunk, chunk_bits, cwo, sub_off);
+    uint64_t lo, hi;
+    span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
+    Prefetch pf;
+    issue_prefetch(pf, pq, lo, last_quad(lo, hi, payload_words), tid0);
+    uint32_t o1[kHalfWords], o2[kHalfWords];
+
+    for (;;) {
+        // the lane index as an opaque value: computations from it are not
+        // hoisted out of the loop to hold dozens of registers across it
+        const uint32_t tid = vgpr_copy(tid0);
+        const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
+        const uint64_t cnt = hi - wbase;
+        const bool staged = span_staged(lo, hi, payload_words, stage_cap);
+        // ---- stage the current group (its loads were issued earlier) --
+        __syncthreads();  // every lane is done with the previous group's rows
+        // wait for the whole prefetch here, on every path (waits left to the
+        // compiler would sit in the branches below, and every later write
+        // of these registers would wait again, for whatever is in flight)
+#pragma unroll
+        for (uint32_t k = 0; k < kPrefetch; ++k) {
+            pin(pf.q[k].x);
+            pin(pf.q[k].y);
+            pin(pf.q[k].z);
+            pin(pf.q[k].w);
+        }
+        if (staged) {
+            const uint32_t nq = (uint32_t)((cnt + 3) / 4);
+            const uint64_t full_q = (payload_words - wbase) / 4;
+#pragma unroll
+            for (uint32_t k = 0; k < kPrefetch; ++k) {
+                const uint32_t q = tid + k * kThreads;
+                if (q < nq && q < full_q) {
+                    const uint32_t i = row_index(4 * q);  // a multiple of 4
+                    stage4[i / 4] = pf.q[k];
+                    if ((q & 7) == 0 && q) stage4[i / 4 - 1] = pf.q[k];  // copies ending the previous row
+                }
+            }
+            if (nq > full_q && tid == (uint32_t)full_q % kThreads) {
+                // the span reaches the payload's last quad, which may be
+                // partial: its words are read one by one
+                uint32_t v[4];
+#pragma unroll
+                for (uint32_t w = 0; w < 4; ++w) {
+                    const uint64_t i = wbase + 4 * full_q + w;
+                    v[w] = i < payload_words ? payload[i] : 0u;
+                }
+                const uint32_t i = row_index(4 * (uint32_t)full_q);
+                const uint4 qv = make_uint4(v[0], v[1], v[2], v[3]);
+                stage4[i / 4] = qv;
+                if ((full_q & 7) == 0 && full_q) stage4[i / 4 - 1] = qv;
+            }
+        }
+        __syncthreads();
+
+        // ---- the next group's entries and payload ----------------------
+        // Loads and prefetch are issued on every pass (for the last, of this
+        // group's own entries and span again): control flow around them
+        // makes the compiler's wait counting conservative, and it then waits
+        // for the prefetch right after issuing it.
+        const uint64_t nxt = grp + gridDim.x;
+        const bool more = nxt < num_full;
+        const uint64_t nxt_c = more ? nxt : grp;
+        const LaneMeta nmeta = load_meta(nxt_c * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
+        const SpanEntries nspan = load_span(nxt_c, num_sub, chunk, num_chunks, cwo, sub_off);
+        uint64_t nlo = 0, nhi = 0, nq_lo = 0, nq_last = 0;
+        const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
+        uint8_t *dst = out + (grp * kThreads + tid) * kSub;
+        const LdsWords src{stage, (uint32_t)((cnt < stage_cap ? cnt : stage_cap) - (cnt > 0 ? 1 : 0))};
+        uint32_t bad = 0;
+        // first half: the next span's bounds after step 5, its payload loads
+        // two per step from step 6
+        uint32_t pos = decode_half<MODE, CHECK>(src, job.pos0, t, bad, o1, [&](uint32_t q) {
+            if (q == 5) {
+                span_words(nspan, payload_words, nlo, nhi);
+                // past the last group: one quad, read by every lane
+                nq_last = more ? last_quad(nlo, nhi, payload_words) : 0;
+                nq_lo = more ? nlo : 0;
+            }
+            if (q >= 6 && q < 6 + kPrefetch / 2) {
+                prefetch_quad(pf, 2 * (q - 6), pq, nq_lo, nq_last, tid);
+                prefetch_quad(pf, 2 * (q - 6) + 1, pq, nq_lo, nq_last, tid);
+            }
+        });
+        // second half: the first half's 128 bytes, 16 per step
+        if (staged) store_half(dst, o1);
+        pos = decode_half<MODE, CHECK>(src, pos, t, bad, o2, [&](uint32_t q) {});
+        if (staged) {
+            if (job.ok && (bad || pos != job.pos_want)) flag_corrupt(status);
+            store_half(dst + kHalf, o2);
+        }
+
+        if (!more) break;
+        grp = nxt;
+        meta = nmeta;
+        lo = nlo;
+        hi = nhi;
+    }
+}
+
 // Main kernel: the full groups (all 256 sub-streams of 256 symbols inside
 // [0, n)) whose span fits the staging rows, so no lane needs masking.  Each
 // half's 128 bytes per lane are stored as soon as they are decoded.  Lanes
@@ -403,104 +549,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const pc_codebook *cbp = reinterpret_cast<const pc_codebook *>(cb);
     load_tables<MODE>(cbb, tab4, area_tab, tid);
     const bool kind_ok = MODE == kDecodeLut12 || cbp->kind == PC_CODEBOOK_QLC;
-    const bool complete = cbp->complete == 1;
     Tables t;
     t.lut = reinterpret_cast<const uint16_t *>(tab4);
     t.sym = reinterpret_cast<const uint8_t *>(tab4);
     t.area = area_tab;
 
-    // ---- prologue: loads of the first group --------------------------
     uint64_t grp = blockIdx.x;
     if (grp >= num_full) return;
-    LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
-    uint64_t lo, hi;
-    span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
-    Prefetch pf;
-    issue_prefetch(pf, payload, payload_words, lo, true, tid);
-    uint32_t o1[kHalfWords], o2[kHalfWords];
-
-    for (;;) {
-        const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
-        const uint64_t cnt = hi - wbase;
-        const bool staged = span_staged(lo, hi, payload_words, stage_cap);
-        // ---- stage the current group (its loads were issued earlier) --
-        __syncthreads();  // every lane is done with the previous group's rows
-        // wait for the whole prefetch here, on every path (waits left to the
-        // compiler would sit in the branches below, and every later write
-        // of these registers would wait again, for whatever is in flight)
-#pragma unroll
-        for (uint32_t k = 0; k < kPrefetch; ++k) {
-            pin(pf.q[k].x);
-            pin(pf.q[k].y);
-            pin(pf.q[k].z);
-            pin(pf.q[k].w);
-        }
-        if (staged) {
-            const uint32_t nq = (uint32_t)((cnt + 3) / 4);
-            const uint64_t full_q = (payload_words - wbase) / 4;
-#pragma unroll
-            for (uint32_t k = 0; k < kPrefetch; ++k) {
-                const uint32_t q = tid + k * kThreads;
-                if (q < nq && q <= full_q) {
-                    uint32_t v[4] = {pf.q[k].x, pf.q[k].y, pf.q[k].z, pf.q[k].w};
-                    if (q == full_q) {  // the words after the last whole quad
-#pragma unroll
-                        for (uint32_t w = 0; w < 4; ++w) {
-                            const uint64_t i = wbase + 4 * full_q + w;
-                            v[w] = i < payload_words ? payload[i] : 0u;
-                        }
-                    }
-                    const uint32_t i = row_index(4 * q);  // a multiple of 4
-                    const uint4 qv = make_uint4(v[0], v[1], v[2], v[3]);
-                    stage4[i / 4] = qv;
-                    if ((q & 7) == 0 && q) stage4[i / 4 - 1] = qv;  // copies ending the previous row
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- the next group's entries (its payload: halfway through) ----
-        // Loads and prefetch are issued on every pass (for the last, of this
-        // group's entries and of one payload line): control flow around
-        // them makes the compiler's wait counting conservative, and it then
-        // waits for the prefetch right after issuing it.
-        const uint64_t nxt = grp + gridDim.x;
-        const bool more = nxt < num_full;
-        const uint64_t nxt_c = more ? nxt : grp;
-        const LaneMeta nmeta = load_meta(nxt_c * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
-        const SpanEntries nspan = load_span(nxt_c, num_sub, chunk, num_chunks, cwo, sub_off);
-        // ---- decode: first half, the next group's payload loads, second half
-        uint64_t nlo = 0, nhi = 0;
-        LaneJob job{false, 0, 0, 0};
-        uint8_t *dst = out + (grp * kThreads + tid) * kSub;
-        const LdsWords src{stage, (uint32_t)(cnt > 0 ? cnt - 1 : 0)};
-        uint32_t bad = 0, pos = 0;
-        if (staged) {
-            job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
-            pos = job.pos0;
-            if (complete)
-                pos = decode_half<MODE, false>(src, pos, t, bad, o1);
-            else
-                pos = decode_half<MODE, true>(src, pos, t, bad, o1);
-            store_half(dst, o1);
-        }
-        span_words(nspan, payload_words, nlo, nhi);
-        issue_prefetch(pf, payload, payload_words, nlo, more, tid);
-        if (staged) {
-            if (complete)
-                pos = decode_half<MODE, false>(src, pos, t, bad, o2);
-            else
-                pos = decode_half<MODE, true>(src, pos, t, bad, o2);
-            if (job.ok && (bad || pos != job.pos_want)) flag_corrupt(status);
-            store_half(dst + kHalf, o2);
-        }
-
-        if (!more) break;
-        grp = nxt;
-        meta = nmeta;
-        lo = nlo;
-        hi = nhi;
-    }
+    if (cbp->complete == 1)
+        decode_groups<MODE, false>(grp, tid, t, kind_ok, stage, stage4, payload, payload_words, chunk_bits, cwo, sub_off,
+                                   n, chunk, num_sub, num_full, num_chunks, out, status, stage_cap);
+    else
+        decode_groups<MODE, true>(grp, tid, t, kind_ok, stage, stage4, payload, payload_words, chunk_bits, cwo, sub_off,
+                                  n, chunk, num_sub, num_full, num_chunks, out, status, stage_cap);
 }
 
 // The groups the main kernel leaves: those whose span exceeds the LDS
