@@ -19,9 +19,10 @@
 //      a few;
 //   2. per lane and per 8 symbols: fetch 4 words at the current bit, funnel
 //      them into a 96-bit window (>= 96 valid bits), then 8 times: read the
-//      16-bit table entry ((32 - length) | symbol << 8) at the top 12 window
-//      bits and advance the window with two funnel shifts (v_alignbit) whose
-//      shift count is the entry itself (the instruction reads 5 bits);
+//      16-bit table entry ((19 - length) | symbol << 8) of the 12 bits at the
+//      current position, take the next entry's offset from the unadvanced
+//      window shifted by the entry, and advance the window with funnel
+//      shifts (v_alignbit) by the entry + 13;
 //   3. every 128 decoded bytes of a lane go out as eight adjacent 16-byte
 //      stores (whole 128-byte lines);
 //   4. the sub-stream must end exactly at the next sub-stream's first bit (or
@@ -78,7 +79,7 @@ struct GlobalWords {
 };
 
 struct Tables {
-    const uint16_t *lut;   // LDS: 4096 x ((32 - length) | symbol << 8), 0 = no codeword
+    const uint16_t *lut;   // LDS: 4096 x ((19 - length) | symbol << 8), 0 = no codeword
     const uint8_t *sym;    // LDS: sym_of_rank[256] (QLC mode)
     const uint32_t *area;  // LDS: per area (index bits | first rank << 8) (QLC mode)
 };
@@ -86,34 +87,47 @@ struct Tables {
 // Decode 8 symbols from the 96-bit window (h, m, l); returns them packed
 // little-endian in two words and adds the bits consumed to pos.  Symbols at
 // index >= lim (masked variant only) consume nothing.
+//
+// Entries (both modes) are (19 - length) | symbol << 8.  In LUT mode the
+// byte offset of the next entry is taken from the window before it is
+// advanced: the 12 bits after a codeword of length len start len bits into
+// h, so (h >> (19 - len)) & 0x1FFE is twice their value, and v_lshrrev reads
+// exactly the 5 low bits of the entry as its count.  The window advance
+// (funnel shifts by 32 - len = entry + 13 in the low 5 bits) then runs
+// beside the next table read instead of before it: per symbol the chain of
+// dependent instructions is one LDS read, one shift and one mask.  (The
+// window has >= 96 valid bits and 7 codewords take <= 84, so the 12 bits
+// after any of the first 7 are valid.)
 template <int MODE, bool MASKED, bool CHECK>
 __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint32_t &pos, uint32_t &bad,
                                         const Tables &t, uint32_t k0, uint32_t lim, uint32_t &o0, uint32_t &o1) {
     uint32_t e[8];
+    uint32_t a = (h >> (31 - kPeek)) & 0x1FFE;  // byte offset of the first entry (LUT mode)
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         uint32_t ek, inv;
         if (MODE == kDecodeLut12) {
-            ek = t.lut[h >> (32 - kPeek)];
+            ek = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(t.lut) + a);
             inv = (ek & 0xFF) == 0;
         } else {
-            const uint32_t a = t.area[h >> 29];
-            const uint32_t b = a & 15;
-            const uint32_t r = (a >> 8) + __builtin_amdgcn_ubfe(h, 29 - b, b);
+            const uint32_t ar = t.area[h >> 29];
+            const uint32_t b = ar & 15;
+            const uint32_t r = (ar >> 8) + __builtin_amdgcn_ubfe(h, 29 - b, b);
             inv = r >= 256;
-            ek = (29 - b) | ((uint32_t)t.sym[r & 255] << 8);
+            ek = (16 - b) | ((uint32_t)t.sym[r & 255] << 8);  // length 3 + b
         }
         if (MASKED && k0 + k >= lim) {
-            ek = (ek & 0xFF00) | 32;  // consumes nothing; the window is kept below
+            ek = (ek & 0xFF00) | 19;  // length 0; the window is kept below
             inv = 0;
         }
         if (CHECK) bad |= inv;
-        // advance by 32 - (ek & 31) = length bits; v_alignbit reads 5 bits of ek
-        const uint32_t h2 = __builtin_amdgcn_alignbit(h, m, ek);
-        const uint32_t m2 = __builtin_amdgcn_alignbit(m, l, ek);
-        const uint32_t l2 = __builtin_amdgcn_alignbit(l, 0u, ek);
-        if (MASKED && (ek & 0xFF) == 32) {
-            // keep the window
+        if (MODE == kDecodeLut12 && k < 7) a = (h >> (ek & 31)) & 0x1FFE;
+        const uint32_t sh = ek + 13;  // 32 - length in the 5 bits v_alignbit reads
+        const uint32_t h2 = __builtin_amdgcn_alignbit(h, m, sh);
+        const uint32_t m2 = __builtin_amdgcn_alignbit(m, l, sh);
+        const uint32_t l2 = __builtin_amdgcn_alignbit(l, 0u, sh);
+        if (MASKED && (ek & 0xFF) == 19) {
+            // keep the window (a funnel shift by 32 would read as 0)
         } else {
             h = h2;
             m = m2;
@@ -121,9 +135,9 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
         }
         e[k] = ek;
     }
-    // each low byte is 32 - length (32 for a masked symbol): 4 of them < 256
+    // each low byte is 19 - length: 4 of them sum below 256
     const uint32_t s0 = (e[0] + e[1] + e[2] + e[3]) & 0xFF, s1 = (e[4] + e[5] + e[6] + e[7]) & 0xFF;
-    pos += 256 - s0 - s1;
+    pos += 8 * 19 - s0 - s1;
     o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
     o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
     // pack and check here: left to the scheduler, the packing sinks towards
@@ -362,12 +376,12 @@ __device__ __forceinline__ void issue_prefetch(Prefetch &pf, gquad *payload, uin
 template <int MODE>
 __device__ __forceinline__ void load_tables(const uint8_t *cbb, uint4 *tab4, uint32_t *area_tab, uint32_t tid) {
     if (MODE == kDecodeLut12) {
-        // 16-bit entries (32 - length) | symbol << 8 (0: no codeword)
+        // 16-bit entries (19 - length) | symbol << 8 (0: no codeword)
         const uint8_t *ds = cbb + kOffDecSym, *dl = cbb + kOffDecSym + 4096;
         uint16_t *lut = reinterpret_cast<uint16_t *>(tab4);
         for (uint32_t i = tid; i < 4096; i += kThreads) {
             const uint32_t len = dl[i];
-            lut[i] = (uint16_t)(len ? ((32 - len) | ((uint32_t)ds[i] << 8)) : 0u);
+            lut[i] = (uint16_t)(len ? ((19 - len) | ((uint32_t)ds[i] << 8)) : 0u);
         }
     } else {
         if (tid < 64)
