@@ -136,6 +136,26 @@ pc_status pc_codebook_validate(const pc_codebook *cb);
  */
 pc_status pc_qlc_optimal_bits(const uint64_t counts[256], uint8_t bits_out[8]);
 
+/*
+ * How well a fixed codebook fits a batch (host, pure).  For the byte
+ * histogram `counts` of the batch:
+ *   *avg_bits = sum(count * length) / sum(count): the payload bits per
+ *               symbol the codebook spends on that batch;
+ *   *entropy  = the batch's Shannon entropy, -sum(p log2 p), in bits per
+ *               symbol: the bound a code built for the batch itself
+ *               approaches.
+ * The single-stage codebook is built once from earlier batches ("Single-
+ * Stage Huffman Encoder for ML Compression", abstract), so avg_bits -
+ * entropy measures how far the batches have drifted from it; the Shannonic
+ * page ("Shannonic: Efficient Entropy-Optimal Compression for ML
+ * Workloads", key observation 1) expects static tables to be refreshed when
+ * the distribution drifts.  A caller rebuilds (pc_codebook_build on the
+ * pooled counts of recent batches) once the gap passes its threshold.
+ * An all-zero histogram gives 0 and 0.  PC_ERR_INVALID_ARG for NULL
+ * pointers or a blob that fails pc_codebook_validate.
+ */
+pc_status pc_codebook_fit(const pc_codebook *cb, const uint64_t counts[256], double *avg_bits, double *entropy);
+
 /* Size queries (host, pure).  chunk must be a valid chunk size, else 0. */
 size_t pc_num_chunks(size_t n, size_t chunk);          /* ceil(n / chunk) */
 size_t pc_num_substreams(size_t n, size_t chunk);      /* sum over chunks of ceil(len_c / 256) */

@@ -23,7 +23,7 @@ CODEBOOK_BYTES = 9536
 SUBSTREAM = 256
 
 EXPORTS = [
-    "pc_status_string", "pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits",
+    "pc_status_string", "pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits", "pc_codebook_fit",
     "pc_num_chunks", "pc_num_substreams", "pc_max_payload_words", "pc_encode_workspace_bytes",
     "pc_encode", "pc_decode", "pc_decode_qlc", "pc_histogram",
 ]
@@ -46,6 +46,7 @@ def _load():
     lib.pc_codebook_build.argtypes = [p, i, p, p]
     lib.pc_codebook_validate.argtypes = [p]
     lib.pc_qlc_optimal_bits.argtypes = [p, p]
+    lib.pc_codebook_fit.argtypes = [p, p, p, p]
     for f in ("pc_num_chunks", "pc_num_substreams", "pc_max_payload_words", "pc_encode_workspace_bytes"):
         getattr(lib, f).argtypes = [sz, sz]
         getattr(lib, f).restype = sz
@@ -53,8 +54,8 @@ def _load():
     lib.pc_decode.argtypes = [p, p, sz, p, p, p, sz, sz, p, p, p]
     lib.pc_decode_qlc.argtypes = [p, p, sz, p, p, p, sz, sz, p, p, p]
     lib.pc_histogram.argtypes = [p, sz, p, p]
-    for f in ("pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits", "pc_encode", "pc_decode",
-              "pc_decode_qlc", "pc_histogram"):
+    for f in ("pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits", "pc_codebook_fit", "pc_encode",
+              "pc_decode", "pc_decode_qlc", "pc_histogram"):
         getattr(lib, f).restype = i
     return lib
 
@@ -120,6 +121,15 @@ def pc_qlc_optimal_bits(counts) -> tuple:
     out = np.zeros(8, dtype=np.uint8)
     _check(lib.pc_qlc_optimal_bits(_ptr(cnt), _ptr(out)), "pc_qlc_optimal_bits")
     return tuple(int(v) for v in out)
+
+
+def pc_codebook_fit(cb: torch.Tensor, counts) -> tuple:
+    """(bits per symbol the codebook spends on a batch with these counts, the batch's entropy)."""
+    cb = cb.cpu().contiguous()
+    cnt = _counts_u64(counts)
+    avg, ent = C.c_double(), C.c_double()
+    _check(lib.pc_codebook_fit(_ptr(cb), _ptr(cnt), C.byref(avg), C.byref(ent)), "pc_codebook_fit")
+    return avg.value, ent.value
 
 
 def pc_num_chunks(n, chunk):

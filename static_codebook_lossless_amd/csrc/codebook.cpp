@@ -6,6 +6,7 @@
 // of e4m3" (abstract, Tables 1 and 2): 8 areas selected by a 3-bit prefix,
 // each with its own fixed index width, over the probability-ranked symbols.
 #include <algorithm>
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 #include <cstring>
@@ -234,6 +235,30 @@ pc_status pc_codebook_validate(const pc_codebook *cb) {
             if (cb->dec_sym[p] != s || cb->dec_len[p] != l) return PC_ERR_INVALID_ARG;
     }
     if (cb->kind == PC_CODEBOOK_QLC && !qlc_bits_ok(cb->qlc_bits)) return PC_ERR_INVALID_ARG;
+    return PC_OK;
+}
+
+pc_status pc_codebook_fit(const pc_codebook *cb, const uint64_t counts[256], double *avg_bits, double *entropy) {
+    if (!counts || !avg_bits || !entropy) return PC_ERR_INVALID_ARG;
+    if (pc_codebook_validate(cb) != PC_OK) return PC_ERR_INVALID_ARG;
+    long double total = 0, bits = 0;
+    for (int s = 0; s < kN; ++s) {
+        total += (long double)counts[s];
+        bits += (long double)counts[s] * cb->length[s];
+    }
+    if (total == 0) {
+        *avg_bits = 0;
+        *entropy = 0;
+        return PC_OK;
+    }
+    long double h = 0;
+    for (int s = 0; s < kN; ++s) {
+        if (!counts[s]) continue;
+        const long double p = (long double)counts[s] / total;
+        h -= p * std::log2(p);
+    }
+    *avg_bits = (double)(bits / total);
+    *entropy = (double)h;
     return PC_OK;
 }
 

@@ -111,3 +111,80 @@ def test_qlc_optimal_bits_on_gelu_beats_table2_layout():
     counts = [int(c) for c in np.bincount(x, minlength=256)]
     bits = pc.pc_qlc_optimal_bits(np.array(counts))
     assert cb.qlc_cost(counts, bits) <= cb.qlc_cost(counts, (1, 3, 3, 3, 3, 5, 6, 7))
+
+
+# ---- codebook fit and refresh (pc_codebook_fit, CodebookRefresh) ----------
+
+@pytest.mark.parametrize("seed", range(12))
+def test_codebook_fit_matches_oracle(seed):
+    rng = np.random.default_rng(500 + seed)
+    build = rng.integers(0, 1 << 20, 256).astype(np.uint64)
+    batch = (rng.integers(0, 1 << 16, 256) * (rng.random(256) < 0.7)).astype(np.uint64)
+    for kind, bits in (("huffman", None), ("qlc", (1, 3, 3, 3, 3, 5, 6, 7))):
+        blob = pc.pc_codebook_build(build, kind, bits)
+        avg, ent = pc.pc_codebook_fit(blob, batch)
+        lengths = cb.codebook([int(c) for c in build], kind, bits)["lengths"]
+        n = int(batch.sum())
+        assert avg == pytest.approx(cb.coded_bits([int(c) for c in batch], lengths) / n, rel=1e-12)
+        assert ent == pytest.approx(cb.entropy_bits([int(c) for c in batch]), rel=1e-12)
+        assert avg >= ent - 1e-12  # no prefix code beats the entropy
+
+
+def test_codebook_fit_closed_forms():
+    blob = pc.pc_codebook_build(np.ones(256, dtype=np.uint64))  # 8 bits for every byte
+    uniform = np.full(256, 7, dtype=np.uint64)
+    assert pc.pc_codebook_fit(blob, uniform) == pytest.approx((8.0, 8.0))
+    two = np.zeros(256, dtype=np.uint64)
+    two[[3, 200]] = 5
+    assert pc.pc_codebook_fit(blob, two) == pytest.approx((8.0, 1.0))
+    dyadic = np.zeros(256, dtype=np.uint64)
+    dyadic[[0, 1, 2, 3]] = [4, 2, 1, 1]  # p = 1/2, 1/4, 1/8, 1/8
+    assert pc.pc_codebook_fit(blob, dyadic)[1] == pytest.approx(1.75)
+    # every byte dyadic (lengths 1, 2, 3, 250 x 11, 3 x 10: Kraft sum 1): the
+    # optimal code has exactly these lengths, so its average is the entropy
+    full = np.array([1024, 512, 256] + [1] * 250 + [2] * 3, dtype=np.uint64)
+    h = (1024 * 1 + 512 * 2 + 256 * 3 + 250 * 11 + 6 * 10) / 2048
+    avg, ent = pc.pc_codebook_fit(pc.pc_codebook_build(full), full)
+    assert ent == pytest.approx(h, rel=1e-12)
+    assert avg == pytest.approx(h, rel=1e-12)
+    assert pc.pc_codebook_fit(blob, np.zeros(256, dtype=np.uint64)) == (0.0, 0.0)
+
+
+def test_codebook_fit_rejects_bad_blob():
+    blob = pc.pc_codebook_build(np.ones(256, dtype=np.uint64)).clone()
+    blob[0] ^= 1  # magic
+    with pytest.raises(pc.PcError):
+        pc.pc_codebook_fit(blob, np.ones(256, dtype=np.uint64))
+
+
+def _e4m3_batch(seed, draw):
+    rng = np.random.default_rng(seed)
+    return np.bincount(W.e4m3_from_f32(draw(rng, 1 << 16).astype(np.float32)), minlength=256).astype(np.uint64)
+
+
+def test_refresh_rebuilds_only_on_drift():
+    normal = lambda rng, n: rng.standard_normal(n)  # noqa: E731
+    heavy = lambda rng, n: rng.standard_t(2, n)     # noqa: E731  (a heavy-tailed drift)
+    r = pc.CodebookRefresh(window=4, threshold=0.02)
+    assert r.observe(_e4m3_batch(1, normal))  # first batch: a codebook is built
+    for s in range(2, 7):  # same distribution, new seeds: the fixed codebook keeps fitting
+        assert not r.observe(_e4m3_batch(s, normal))
+        avg, ent = r.last_fit
+        assert (avg - ent) / ent < 0.02
+    drifted = _e4m3_batch(7, heavy)
+    before = pc.pc_codebook_fit(r.codebook, drifted)
+    assert r.observe(drifted)  # the gap grew past the threshold: rebuilt
+    assert r.rebuilds == 2
+    # the rebuilt codebook pools the window (3 old batches + the drifted one)
+    pooled = r.pooled()
+    assert pc.codebook_fields(r.codebook)["length"].tolist() == cb.codebook([int(c) for c in pooled])["lengths"]
+    after = pc.pc_codebook_fit(r.codebook, drifted)
+    assert after[0] < before[0]
+
+
+def test_refresh_qlc_widths_follow_the_pool():
+    r = pc.CodebookRefresh(kind="qlc")
+    c = _e4m3_batch(11, lambda rng, n: rng.standard_normal(n))
+    assert r.observe(c)
+    f = pc.codebook_fields(r.codebook)
+    assert tuple(f["qlc_bits"].tolist()) == pc.pc_qlc_optimal_bits(c)
