@@ -10,9 +10,9 @@
 // persistent and walk the groups with a stride of the grid size.  While a
 // workgroup decodes group k out of LDS, the loads of group k+1 (its
 // container entries, then its payload span into registers, two 16-byte
-// loads per lane after each of the steps 6-13 of the first 128 symbols) are
+// loads per lane after each of the steps 6-14 of the first 128 symbols) are
 // in flight, so HBM latency is hidden behind decoding.  Per group:
-//   1. the staged span sits in LDS in rows of 36 words: 32 payload words plus
+//   1. the staged span sits in LDS in rows of 68 words: 64 payload words plus
 //      copies of the next row's first four, so any 4-word window read stays
 //      in one row, rows start 16-byte aligned, and lanes whose sub-streams
 //      start ~50 words apart spread over the LDS banks instead of falling on
@@ -38,13 +38,14 @@ namespace pc {
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint32_t kRow = 32;     // payload words per LDS row
-constexpr uint32_t kRowPad = 36;  // row + copies of the next row's first 4 words
-// Staged span: up to 64 KiB of payload (8 bits per symbol; 16 x 16 B per
-// lane in flight), so that two workgroups fit in a CU's LDS.
-constexpr uint32_t kPrefetch = 16;
-constexpr uint32_t kMaxStageWords = kPrefetch * 4 * kThreads;  // 16384
-constexpr uint32_t kStageRows = 508;
+constexpr uint32_t kRow = 64;     // payload words per LDS row
+constexpr uint32_t kRowPad = 68;  // row + copies of the next row's first 4 words
+// Staged span: up to 16512 words of payload, enough for a group at 8 bits
+// per symbol (16384 words) from a row-aligned start (17 x 16 B per lane in
+// flight), with two workgroups in a CU's LDS.
+constexpr uint32_t kPrefetch = 17;
+constexpr uint32_t kMaxStageWords = kPrefetch * 4 * kThreads;  // 17408
+constexpr uint32_t kStageRows = 258;
 static_assert(kStageRows * kRow <= kMaxStageWords, "prefetch covers the staged span");
 constexpr uint32_t kGroupsPerCU = 2;
 
@@ -52,7 +53,7 @@ __device__ __forceinline__ void flag_corrupt(uint32_t *status) {
     atomicCAS(status, 0u, (uint32_t)PC_ERR_CORRUPT);
 }
 
-__device__ __forceinline__ uint32_t row_index(uint32_t a) { return a + 4 * (a >> 5); }
+__device__ __forceinline__ uint32_t row_index(uint32_t a) { return a + 4 * (a >> 6); }
 
 // Payload word sources.  Indices are clamped so that corrupt positions never
 // read outside the staged words or the payload.
@@ -475,7 +476,7 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
                 if (q < nq && q < full_q) {
                     const uint32_t i = row_index(4 * q);  // a multiple of 4
                     stage4[i / 4] = pf.q[k];
-                    if ((q & 7) == 0 && q) stage4[i / 4 - 1] = pf.q[k];  // copies ending the previous row
+                    if ((q & 15) == 0 && q) stage4[i / 4 - 1] = pf.q[k];  // copies ending the previous row
                 }
             }
             if (nq > full_q && tid == (uint32_t)full_q % kThreads) {
@@ -490,7 +491,7 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
                 const uint32_t i = row_index(4 * (uint32_t)full_q);
                 const uint4 qv = make_uint4(v[0], v[1], v[2], v[3]);
                 stage4[i / 4] = qv;
-                if ((full_q & 7) == 0 && full_q) stage4[i / 4 - 1] = qv;
+                if ((full_q & 15) == 0 && full_q) stage4[i / 4 - 1] = qv;
             }
         }
         __syncthreads();
@@ -519,10 +520,8 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
                 nq_last = more ? last_quad(nlo, nhi, payload_words) : 0;
                 nq_lo = more ? nlo : 0;
             }
-            if (q >= 6 && q < 6 + kPrefetch / 2) {
-                prefetch_quad(pf, 2 * (q - 6), pq, nq_lo, nq_last, tid);
-                prefetch_quad(pf, 2 * (q - 6) + 1, pq, nq_lo, nq_last, tid);
-            }
+            if (q >= 6 && 2 * (q - 6) < kPrefetch) prefetch_quad(pf, 2 * (q - 6), pq, nq_lo, nq_last, tid);
+            if (q >= 6 && 2 * (q - 6) + 1 < kPrefetch) prefetch_quad(pf, 2 * (q - 6) + 1, pq, nq_lo, nq_last, tid);
         });
         // second half: the first half's 128 bytes, 16 per step
         if (staged) store_half(dst, o1);
@@ -581,9 +580,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 // The groups the main kernel leaves: those whose span exceeds the LDS
 // budget (the same span test picks them) and the last group when it is not
 // full.  Each lane reads its words straight from global memory and writes
-// only bytes below its symbol count.  The first wave of a workgroup tests 64 groups at once (one per
-// lane), then the workgroup decodes the ones that were not staged, so that
-// a stream with no such group costs one round of entry loads.
+// only bytes below its symbol count.  Workgroup b owns the groups b, b + G,
+// b + 2G, ... (G workgroups); its first wave tests 64 of them at once (one
+// per lane), then the workgroup decodes the ones that were not staged, so
+// that a stream with no such group costs one round of entry loads, and a
+// stream of such groups is spread over all workgroups.
 constexpr uint32_t kTestBatch = 64;
 
 template <int MODE>
@@ -606,15 +607,16 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     t.lut = reinterpret_cast<const uint16_t *>(tab4);
     t.sym = reinterpret_cast<const uint8_t *>(tab4);
     t.area = area_tab;
-    for (uint64_t base = (uint64_t)blockIdx.x * kTestBatch; base < num_groups;
-         base += (uint64_t)gridDim.x * kTestBatch) {
+    const uint64_t G = gridDim.x;
+    for (uint64_t base = blockIdx.x; base < num_groups; base += G * kTestBatch) {
+        // this batch: groups base + l G, l = 0 .. 63
         if (tid == 0) ntodo = 0;
         __syncthreads();
-        if (tid < kTestBatch && base + tid < num_groups) {
+        if (tid < kTestBatch && base + tid * G < num_groups) {
+            const uint64_t g = base + tid * G;
             uint64_t lo, hi;
-            span_words_lane(load_span(base + tid, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
-            if (base + tid >= num_full || !span_staged(lo, hi, payload_words, stage_cap))
-                todo[atomicAdd(&ntodo, 1u)] = tid;
+            span_words_lane(load_span(g, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
+            if (g >= num_full || !span_staged(lo, hi, payload_words, stage_cap)) todo[atomicAdd(&ntodo, 1u)] = tid;
         }
         __syncthreads();
         const uint32_t nt = ntodo;
@@ -624,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
             loaded = true;
         }
         for (uint32_t i = 0; i < nt; ++i) {
-            const uint64_t grp = base + todo[i];
+            const uint64_t grp = base + todo[i] * G;
             uint64_t lo, hi;
             span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
             const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
@@ -652,10 +654,9 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     const uint64_t last = n - (nc - 1) * chunk;
     const uint64_t num_sub = (nc - 1) * (chunk / kSub) + (last + kSub - 1) / kSub;
     const uint64_t num_groups = (num_sub + kThreads - 1) / kThreads;
-    // LDS budget for a staged span: always the largest that lets two
-    // workgroups share a CU's 160 KiB (two per CU is the occupancy the
-    // kernel's registers allow anyway): 508 rows of 36 words beside the 8 KiB
-    // table, i.e. up to 16256 payload words (7.9 bits per symbol).
+    // LDS budget for a staged span: two workgroups share a CU's 160 KiB:
+    // 258 rows of 68 words beside the 8 KiB table, i.e. up to 16512 payload
+    // words (8 bits per symbol from a row-aligned start).
     const uint64_t cap = kStageRows * kRow;
     const size_t shmem = kStageRows * kRowPad * 4;
     static bool attr_set[2] = {false, false};
@@ -680,7 +681,7 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     uint64_t grid = (uint64_t)num_cus * kGroupsPerCU;
     if (grid > num_full) grid = num_full;
     uint64_t grid_g = (uint64_t)num_cus * kGroupsPerCU;
-    if (grid_g > (num_groups + kTestBatch - 1) / kTestBatch) grid_g = (num_groups + kTestBatch - 1) / kTestBatch;
+    if (grid_g > num_groups) grid_g = num_groups;
     if (num_sub >= 0xFFFFFFFFull) return hipErrorInvalidValue;
 #define PC_DEC(K)                                                                                             \
     hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), shmem, stream, cb, payload, payload_words,     \

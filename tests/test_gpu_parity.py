@@ -211,6 +211,27 @@ def test_degenerate_data(kind):
         roundtrip(dcb, obook, x_np, 4096, qlc_decoder=(kind == "qlc"))
 
 
+@pytest.mark.parametrize("chunk", [4096, 16384, 65536])
+def test_incompressible_data(chunk):
+    """Uniform random bytes under the code of their own (flat) histogram: 8
+    bits per symbol, the most a staged group may hold (a group's span is
+    16384 words), and with one byte value made rarer, 8+ bits for some
+    groups (decoded from global memory)."""
+    rng = np.random.default_rng(77)
+    n = 3 * 65536 + 1000
+    x_np = rng.integers(0, 256, n, dtype=np.uint8)
+    say("incompressible: flat code, chunk", chunk)
+    dcb, obook = make_book(np.full(256, 1000, dtype=np.int64), "huffman", None)
+    assert set(obook["lengths"]) == {8}
+    roundtrip(dcb, obook, x_np, chunk)
+    say("incompressible: skewed code, chunk", chunk)
+    counts = np.full(256, 1000, dtype=np.int64)
+    counts[:2] = 10  # two 9-bit codes (and shorter ones elsewhere)
+    dcb, obook = make_book(counts, "huffman", None)
+    assert max(obook["lengths"]) > 8
+    roundtrip(dcb, obook, x_np, chunk)
+
+
 # --------------------------------------------------------------------------
 # corruption: the decoder's status must agree with the oracle decoder's and
 # nothing outside [0, n) may be written
