@@ -510,13 +510,14 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
                        (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws)
     // Chunks of 1, 2 or 4 tiles of 16K symbols use 1024-lane workgroups, 4K
     // and 8K symbol chunks 256 lanes.  The LDS output buffer holds a whole
-    // chunk at 12 bits per symbol, except for 64K chunks (8 bits per symbol,
-    // so that two workgroups fit in a CU).  Any other chunk size, and a short
+    // chunk at 12 bits per symbol, except for 64K chunks (8 bits per symbol
+    // plus the 64-bit margin of the fit test, so that two workgroups fit in
+    // a CU).  Any other chunk size, and a short
     // last chunk (launched after the full ones, so its look-back finds its
     // predecessor finished), go to the re-reading kernel.
     bool fast = true;
     if (nfull == 0) fast = false;
-    else if (chunk == 65536) PC_ENC(1024, 4, 16384);
+    else if (chunk == 65536) PC_ENC(1024, 4, 16392);
     else if (chunk == 32768) PC_ENC(1024, 2, 12288);
     else if (chunk == 16384) PC_ENC(1024, 1, 6144);
     else if (chunk == 8192) PC_ENC(256, 2, 3072);
