@@ -38,9 +38,10 @@ __device__ __forceinline__ void st_desc(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Exclusive prefix (in words) of chunk c over all earlier chunks.  Called by
-// one whole wave.  Chunk c's workgroup got ticket c from an atomic counter,
-// so every earlier chunk's workgroup is already running and will publish.
+// Exclusive prefix (in words) of descriptor c over all earlier ones (a
+// descriptor covers the chunks of one workgroup, in chunk order).  Called by
+// one whole wave.  The workgroup got ticket c from an atomic counter, so
+// every earlier descriptor's workgroup is already running and will publish.
 // Each round reads 128 predecessors (2 per lane, nearest first) in one trip
 // to memory and polls, without pausing, until all have published; it then
 // sums counts up to the nearest inclusive prefix, or walks 128 chunks
@@ -205,17 +206,19 @@ __device__ __forceinline__ void flush_tile(SH &sh, uint32_t *dst, uint32_t tile_
 }
 
 // ---------------------------------------------------------------------------
-// Whole-chunk kernel (chunks of exactly NT tiles of THREADS x 16 symbols).
+// Whole-chunk kernel: a workgroup encodes NT tiles of THREADS x 16 symbols,
+// NT / TPC consecutive chunks of exactly TPC tiles each.
 //
 // Every symbol is looked up once: the table entry is code << 16 | length.
 // Per tile, each lane turns its 16 symbols into 4 groups (<= 48 bits each),
 // the tile's bit offsets come from a wave scan plus a scan of the wave
 // totals, and the groups are ORed straight into an LDS buffer that holds the
-// whole chunk's output.  After the last tile the chunk's size is known; the
-// cross-chunk scan (look-back) gives its word offset and the buffer is stored
-// in one coalesced pass.  A chunk whose output would not fit the buffer
-// (more than BUFW words: only data that does not compress) is redone tile by
-// tile with a store per tile.
+// workgroup's whole output, each chunk starting on a new word.  After the
+// last tile the size is known; one cross-workgroup scan (look-back) gives
+// the word offset of the first chunk and the buffer is stored in one
+// coalesced pass.  Output that would not fit the buffer (more than BUFW
+// words: only data that does not compress) is redone tile by tile with a
+// store per tile.
 // ---------------------------------------------------------------------------
 
 template <uint32_t THREADS, int NT, uint32_t BUFW>
@@ -277,7 +280,7 @@ __device__ __forceinline__ void tile_offsets(const uint32_t *wave_tot, uint32_t 
     total = (uint32_t)__builtin_amdgcn_readlane((int)vs, (int)NW - 1);
 }
 
-template <uint32_t THREADS, int NT, uint32_t BUFW>
+template <uint32_t THREADS, int NT, uint32_t BUFW, int TPC>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS == 1024 ? 8 : 1))) void encode_chunk_kernel(
     const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint64_t n, uint32_t chunk,
     uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
@@ -285,6 +288,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
     using SH = ChunkShared<THREADS, NT, BUFW>;
     constexpr uint32_t TILE = THREADS * kSymPerLane;
     constexpr uint32_t NW = THREADS / 64;
+    constexpr int NC = NT / TPC;  // chunks per workgroup
+    static_assert(NT % TPC == 0, "whole chunks per workgroup");
     __shared__ SH sh;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) sh.misc[0] = atomicAdd(reinterpret_cast<uint32_t *>(ws), 1u);
@@ -294,18 +299,29 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
     }
     for (uint32_t i = tid; i < (BUFW + 8) / 4; i += THREADS) reinterpret_cast<uint4 *>(sh.buf)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
-    const uint32_t c = uniform(sh.misc[0]);
-    const uint64_t base = (uint64_t)c * chunk;
-    const uint8_t *src = in + base + tid * 16;
-    uint32_t *so = sub_off + (uint64_t)c * (chunk / kSub);
+    const uint32_t s = uniform(sh.misc[0]);  // the workgroup's look-back index
+    const uint32_t c0 = s * NC;               // its first chunk
+    const uint8_t *src = in + (uint64_t)c0 * chunk + tid * 16;
+    uint32_t *so = sub_off + (uint64_t)c0 * (chunk / kSub);
 
     // ---- one pass: lookups, offsets, packing into the chunk buffer -------
-    // (the next tile's 16 bytes are in flight while a tile is processed)
-    uint32_t tbase = 0;
+    // (the next tile's 16 bytes are in flight while a tile is processed).
+    // Chunk k of the workgroup starts at word cw[k] of the buffer; tbase
+    // counts bits from the current chunk's start.
+    uint32_t tbase = 0, cword = 0;
+    uint32_t cw[NC], cbits[NC];
     bool fits = true;
     uint4 xn = load_stream16(src);
 #pragma unroll
     for (int r = 0; r < NT; ++r) {
+        if (r % TPC == 0) {
+            if (r) {
+                cbits[r / TPC - 1] = tbase;
+                cword = uniform(cword + ((tbase + 31) >> 5));
+                tbase = 0;
+            }
+            cw[r / TPC] = cword;
+        }
         const uint4 xc = xn;
         if (r + 1 < NT) xn = load_stream16(src + (r + 1) * TILE);
         uint64_t g[4];
@@ -319,11 +335,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
         tile_offsets<NW>(sh.wave_tot[r], lane, wave, before, ttot);
         const uint32_t my = tbase + before + incl - bits;
         if ((tid & 15) == 0) so[(r * TILE + tid * kSymPerLane) / kSub] = my;
-        if (tbase + ttot + 64 > BUFW * 32) {
+        if (cword * 32 + tbase + ttot + 64 > BUFW * 32) {
             fits = false;
             break;
         }
-        uint32_t p = my;
+        uint32_t p = cword * 32 + my;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             place_group(g[q], ng[q], p, sh.buf);
@@ -333,17 +349,20 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
     }
 
     if (fits) {
-        const uint32_t total = tbase;
-        const uint64_t words = (total + 31) >> 5;
+        cbits[NC - 1] = tbase;
+        const uint64_t words = cword + ((tbase + 31) >> 5);
         __syncthreads();
         if (wave == 0) {
-            const uint64_t excl = lookback(ws + 1, c, words, lane);
+            const uint64_t excl = lookback(ws + 1, s, words, lane);
             if (lane == 0) {
                 sh.misc[1] = (uint32_t)excl;
                 sh.misc[2] = (uint32_t)(excl >> 32);
-                chunk_bits[c] = total;
-                cwo[c] = excl;
-                if (c == num_chunks - 1) cwo[num_chunks] = excl + words;
+#pragma unroll
+                for (int k = 0; k < NC; ++k) {
+                    chunk_bits[c0 + k] = cbits[k];
+                    cwo[c0 + k] = excl + cw[k];
+                }
+                if (c0 + NC == num_chunks) cwo[num_chunks] = excl + words;
             }
         }
         __syncthreads();
@@ -352,7 +371,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
         return;
     }
 
-    // ---- the chunk does not fit: offsets of all tiles, then tile by tile --
+    // ---- the chunks do not fit: offsets of all tiles, then tile by tile --
+    // tb[r]: bit of the workgroup's output where tile r starts (each chunk
+    // starts on a word)
     uint32_t tb[NT + 1], e[NT];
     tb[0] = 0;
 #pragma unroll
@@ -368,20 +389,30 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
         uint32_t before, ttot;
         tile_offsets<NW>(sh.wave_tot[r], lane, wave, before, ttot);
         e[r] = before + incl - bits;
-        tb[r + 1] = uniform(tb[r] + ttot);
-        if ((tid & 15) == 0) so[(r * TILE + tid * kSymPerLane) / kSub] = tb[r] + e[r];
+        const uint32_t cstart = tb[r - r % TPC];  // the chunk's first bit (a word boundary)
+        if ((tid & 15) == 0) so[(r * TILE + tid * kSymPerLane) / kSub] = tb[r] - cstart + e[r];
+        const uint32_t end = uniform(tb[r] + ttot);
+        if (r % TPC == TPC - 1) {
+            cbits[r / TPC] = end - cstart;
+            cw[r / TPC] = cstart >> 5;
+            tb[r + 1] = (end + 31) & ~31u;
+        } else {
+            tb[r + 1] = end;
+        }
     }
-    const uint32_t total = tb[NT];
-    const uint64_t words = (total + 31) >> 5;
+    const uint64_t words = tb[NT] >> 5;
     for (uint32_t i = tid; i < (BUFW + 8) / 4; i += THREADS) reinterpret_cast<uint4 *>(sh.buf)[i] = make_uint4(0, 0, 0, 0);
     if (wave == 0) {
-        const uint64_t excl = lookback(ws + 1, c, words, lane);
+        const uint64_t excl = lookback(ws + 1, s, words, lane);
         if (lane == 0) {
             sh.misc[1] = (uint32_t)excl;
             sh.misc[2] = (uint32_t)(excl >> 32);
-            chunk_bits[c] = total;
-            cwo[c] = excl;
-            if (c == num_chunks - 1) cwo[num_chunks] = excl + words;
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                chunk_bits[c0 + k] = cbits[k];
+                cwo[c0 + k] = excl + cw[k];
+            }
+            if (c0 + NC == num_chunks) cwo[num_chunks] = excl + words;
         }
     }
     __syncthreads();
@@ -398,10 +429,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
             p += ng[q];
         }
         __syncthreads();
+        // a chunk's last tile ends with its partial word (the next chunk
+        // starts on a new word); other tiles carry it to the next
+        const bool last = r % TPC == TPC - 1;
+        const uint32_t tend = last ? (uint32_t)(cw[r / TPC] * 32 + cbits[r / TPC]) : tb[r + 1];
         const uint32_t first_word = tb[r] >> 5;
-        const bool last = r + 1 == NT;
-        const uint32_t nfull = (tb[r + 1] >> 5) - first_word;
-        const uint32_t nstore = last ? ((tb[r + 1] + 31) >> 5) - first_word : nfull;
+        const uint32_t nfull = (tend >> 5) - first_word;
+        const uint32_t nstore = last ? ((tend + 31) >> 5) - first_word : nfull;
         for (uint32_t i = tid; i < nstore; i += THREADS) dst[first_word + i] = sh.buf[i];
         const uint32_t carry = sh.buf[nfull];
         __syncthreads();
@@ -412,10 +446,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
 
 // Any chunk size: the counting pass and the packing pass each read the
 // chunk (the second read is served by the caches for moderate chunks).
+// A workgroup's ticket t is its look-back index; it encodes chunk t + coff
+// (coff > 0 when a launch of multi-chunk workgroups went first).
 __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint64_t n, uint32_t chunk,
     uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
-    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws) {
+    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws, uint32_t coff) {
     using SH = Shared<kThreads>;
     __shared__ SH sh;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -427,7 +463,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     }
     for (uint32_t i = tid; i < SH::kStage; i += kThreads) sh.stage[i] = 0;
     __syncthreads();
-    const uint32_t c = uniform(sh.misc[0]);
+    const uint32_t t = uniform(sh.misc[0]);
+    const uint32_t c = t + coff;
     const uint64_t base = (uint64_t)c * chunk;
     const uint32_t lenc = (uint32_t)((n - base) < chunk ? (n - base) : chunk);
     const uint32_t ntiles = (lenc + kTile - 1) / kTile;
@@ -443,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     const uint32_t total = uniform(sh.wave_tot[0][0] + sh.wave_tot[0][1] + sh.wave_tot[0][2] + sh.wave_tot[0][3]);
     const uint64_t words = (total + 31) >> 5;
     if (wave == 0) {
-        const uint64_t excl = lookback(ws + 1, c, words, lane);
+        const uint64_t excl = lookback(ws + 1, t, words, lane);
         if (lane == 0) {
             sh.misc[1] = (uint32_t)excl;
             sh.misc[2] = (uint32_t)(excl >> 32);
@@ -502,31 +539,44 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
     hipLaunchKernelGGL(encode_init_kernel, dim3(init_blocks ? init_blocks : 1), dim3(256), 0, stream, ws,
                        ws_words, cwo, n == 0 ? 1 : 0);
     if (n == 0) return hipGetLastError();
-    const uint64_t nfull = n / chunk;           // chunks of exactly `chunk` symbols
-    const bool short_last = nfull != nc;
-    const dim3 grid((uint32_t)nfull);
-#define PC_ENC(T, NT, BW)                                                                                  \
-    hipLaunchKernelGGL((encode_chunk_kernel<T, NT, BW>), grid, dim3(T), 0, stream, cb, in, n, chunk,         \
-                       (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws)
-    // Chunks of 1, 2 or 4 tiles of 16K symbols use 1024-lane workgroups, 4K
-    // and 8K symbol chunks 256 lanes.  The LDS output buffer holds a whole
-    // chunk at 12 bits per symbol, except for 64K chunks (8 bits per symbol
-    // plus the 64-bit margin of the fit test, so that two workgroups fit in
-    // a CU).  Any other chunk size, and a short
-    // last chunk (launched after the full ones, so its look-back finds its
-    // predecessor finished), go to the re-reading kernel.
-    bool fast = true;
-    if (nfull == 0) fast = false;
-    else if (chunk == 65536) PC_ENC(1024, 4, 16392);
-    else if (chunk == 32768) PC_ENC(1024, 2, 12288);
-    else if (chunk == 16384) PC_ENC(1024, 1, 6144);
-    else if (chunk == 8192) PC_ENC(256, 2, 3072);
-    else if (chunk == 4096) PC_ENC(256, 1, 1536);
-    else fast = false;
-    const uint64_t rest = fast ? (short_last ? 1 : 0) : nc;
+    const uint64_t nfull = n / chunk;  // chunks of exactly `chunk` symbols
+    // Full chunks go to workgroups of NT tiles (TPC tiles per chunk, so
+    // NT / TPC consecutive chunks and one look-back per workgroup); the
+    // full chunks left over and a short last chunk go to the re-reading
+    // kernel, launched after them, so their look-backs find every
+    // predecessor finished.  The 1024-lane kernels hold 64K symbols per
+    // workgroup; the LDS output buffer holds them at 8 bits per symbol plus
+    // the padding words between chunks and the 64-bit margin of the fit
+    // test (two such workgroups fit a CU).  4K and 8K symbol chunks take
+    // 256-lane workgroups of 32K symbols when there are many of them, else
+    // one chunk per workgroup, so that a small input still spreads over the
+    // CUs (the 1-chunk buffers hold 12 bits per symbol).
+    constexpr uint64_t kManySmall = 8192;
+    uint64_t done = 0, tickets = 0;  // chunks and workgroups of the multi-chunk launch
+#define PC_ENC(T, NT, BW, TPC)                                                                             \
+    do {                                                                                                   \
+        const uint64_t nsup = nfull / ((NT) / (TPC));                                                      \
+        if (nsup) {                                                                                        \
+            hipLaunchKernelGGL((encode_chunk_kernel<T, NT, BW, TPC>), dim3((uint32_t)nsup), dim3(T), 0,    \
+                               stream, cb, in, n, chunk, (uint32_t)nc, payload, chunk_bits, cwo, sub_off,  \
+                               ws);                                                                        \
+            done = nsup * ((NT) / (TPC));                                                                  \
+            tickets = nsup;                                                                                \
+        }                                                                                               \
+    } while (0)
+    if (chunk == 65536) PC_ENC(1024, 4, 16392, 4);
+    else if (chunk == 32768) PC_ENC(1024, 4, 16392, 2);
+    else if (chunk == 16384) PC_ENC(1024, 4, 16392, 1);
+    else if (chunk == 8192 && nfull >= kManySmall) PC_ENC(256, 8, 8200, 2);
+    else if (chunk == 8192) PC_ENC(256, 2, 3072, 2);
+    else if (chunk == 4096 && nfull >= kManySmall) PC_ENC(256, 8, 8200, 1);
+    else if (chunk == 4096) PC_ENC(256, 1, 1536, 1);
+    const uint64_t rest = nc - done;
+    // tickets continue from the multi-chunk launch's: ticket t encodes
+    // chunk t + done - tickets
     if (rest)
         hipLaunchKernelGGL(encode_kernel_any, dim3((uint32_t)rest), dim3(kThreads), 0, stream, cb, in, n, chunk,
-                           (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws);
+                           (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws, (uint32_t)(done - tickets));
 #undef PC_ENC
     return hipGetLastError();
 }

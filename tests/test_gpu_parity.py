@@ -148,11 +148,15 @@ def random_counts(seed):
     return (rng.pareto(1.1, 256) * 1000).astype(np.int64)
 
 
-@pytest.mark.parametrize("chunk", [256, 768, 4096, 16384, 65536, 131072])
+@pytest.mark.parametrize("chunk", [256, 768, 4096, 8192, 16384, 32768, 65536, 131072])
 def test_edge_sizes(chunk):
+    """Sizes around one chunk, and runs of chunks that fill the multi-chunk
+    workgroups (up to 8 chunks each) exactly, or leave whole chunks and a
+    short chunk over for the re-reading kernel."""
     for kind, bits in (("huffman", None), ("qlc", (1, 3, 3, 3, 3, 5, 6, 7))):
         dcb, obook = make_book(random_counts(chunk), kind, bits)
-        sizes = sorted({0, 1, 255, 256, 257, chunk - 1, chunk, chunk + 1, 3 * chunk + 100})
+        sizes = sorted({0, 1, 255, 256, 257, chunk - 1, chunk, chunk + 1, 3 * chunk + 100, 8 * chunk,
+                        11 * chunk + 100})
         for n in sizes:
             say("edge size:", kind, "chunk", chunk, "n", n)
             x_np = skewed(n, n + chunk)
@@ -187,6 +191,23 @@ def test_many_chunks_lookback():
     roundtrip(dcb, obook, x_np, 256)
 
 
+@pytest.mark.parametrize("chunk", [4096, 8192])
+def test_many_small_chunks(chunk):
+    """8195 chunks and a short one: enough small chunks for the encoder's
+    multi-chunk workgroups (32K symbols each) with whole chunks and a short
+    chunk left over.  Every fifth 32K block is uniform bytes (~9.8 bits per
+    symbol under this code), so those workgroups' output overflows the LDS
+    buffer and takes the tile-by-tile path."""
+    dcb, obook = make_book(np.bincount(skewed(1 << 20, 99), minlength=256))  # ~4.9 bits on skewed data
+    n = 8195 * chunk + 100
+    x_np = skewed(n, 12)
+    blocks = x_np[: (n // 32768) * 32768].reshape(-1, 32768)
+    rng = np.random.default_rng(13)
+    blocks[::5] = rng.integers(0, 256, blocks[::5].shape, dtype=np.uint8)
+    say("many small chunks:", chunk, "n", n)
+    roundtrip(dcb, obook, x_np, chunk)
+
+
 @pytest.mark.parametrize("kind", ["huffman", "qlc"])
 def test_degenerate_data(kind):
     bits = (1, 3, 3, 3, 3, 5, 6, 7) if kind == "qlc" else None
@@ -211,7 +232,7 @@ def test_degenerate_data(kind):
         roundtrip(dcb, obook, x_np, 4096, qlc_decoder=(kind == "qlc"))
 
 
-@pytest.mark.parametrize("chunk", [4096, 16384, 65536])
+@pytest.mark.parametrize("chunk", [4096, 8192, 16384, 32768, 65536])
 def test_incompressible_data(chunk):
     """Uniform random bytes under the code of their own (flat) histogram: 8
     bits per symbol, the most a staged group may hold (a group's span is
