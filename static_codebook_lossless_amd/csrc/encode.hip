@@ -54,12 +54,18 @@ __device__ __forceinline__ void st_desc(uint64_t *p, uint64_t v) {
 constexpr uint32_t kMaxPolls = 1u << 20;
 constexpr int kLookWin = 2;  // descriptors per lane per round
 
-__device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_t lane) {
+// Publish descriptor c's own count: inclusive for c == 0, else aggregate.
+__device__ __forceinline__ void publish_count(uint64_t *desc, uint32_t c, uint64_t words) {
+    st_desc(&desc[c], (c == 0 ? kDescInclusive : kDescAggregate) | words);
+}
+
+// `published`: the caller already ran publish_count for c.
+__device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_t lane, bool published = false) {
     if (c == 0) {
-        if (lane == 0) st_desc(&desc[0], kDescInclusive | words);
+        if (lane == 0 && !published) st_desc(&desc[0], kDescInclusive | words);
         return 0;
     }
-    if (lane == 0) st_desc(&desc[c], kDescAggregate | words);
+    if (lane == 0 && !published) st_desc(&desc[c], kDescAggregate | words);
     uint64_t excl = 0;
     int64_t idx = (int64_t)c - 1;
     while (true) {
@@ -307,9 +313,14 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
     // ---- one pass: lookups, offsets, packing into the chunk buffer -------
     // (the next tile's 16 bytes are in flight while a tile is processed).
     // Chunk k of the workgroup starts at word cw[k] of the buffer; tbase
-    // counts bits from the current chunk's start.
+    // counts bits from the current chunk's start.  The last kHold tiles are
+    // placed only after the workgroup's word count has been published
+    // (their groups wait in registers, two groups of <= 48 bits in three
+    // words), so successors' look-backs see the count earlier.
+    constexpr int kHold = NC == 1 ? 1 : 0;  // (more held tiles, or several chunks, spill registers)
     uint32_t tbase = 0, cword = 0;
     uint32_t cw[NC], cbits[NC];
+    uint32_t HG[kHold + 1][6], HN[kHold + 1], HP[kHold + 1];  // held tiles: groups, lengths, first bit
     bool fits = true;
     uint4 xn = load_stream16(src);
 #pragma unroll
@@ -340,10 +351,25 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
             break;
         }
         uint32_t p = cword * 32 + my;
+        if (r < NT - kHold) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            place_group(g[q], ng[q], p, sh.buf);
-            p += ng[q];
+            for (int q = 0; q < 4; ++q) {
+                place_group(g[q], ng[q], p, sh.buf);
+                p += ng[q];
+            }
+        } else {
+            const int hr = r - (NT - kHold);  // unrolled: a constant
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                HG[hr][3 * h] = (uint32_t)g[2 * h];
+                HG[hr][3 * h + 1] = (uint32_t)g[2 * h + 1];
+                HG[hr][3 * h + 2] = (uint32_t)(g[2 * h] >> 32) | (uint32_t)(g[2 * h + 1] >> 32) << 16;
+            }
+            // formed here, not kept as table entries
+            asm volatile("" : "+v"(HG[hr][0]), "+v"(HG[hr][1]), "+v"(HG[hr][2]), "+v"(HG[hr][3]), "+v"(HG[hr][4]),
+                         "+v"(HG[hr][5]));
+            HN[hr] = ng[0] | ng[1] << 8 | ng[2] << 16 | ng[3] << 24;
+            HP[hr] = p;
         }
         tbase = uniform(tbase + ttot);
     }
@@ -351,9 +377,23 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
     if (fits) {
         cbits[NC - 1] = tbase;
         const uint64_t words = cword + ((tbase + 31) >> 5);
+        if (kHold && tid == 0) publish_count(ws + 1, s, words);
+#pragma unroll
+        for (int hr = 0; hr < kHold; ++hr) {
+            uint32_t p = HP[hr];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t h = q >> 1;
+                const uint32_t hi = (q & 1) ? HG[hr][3 * h + 2] >> 16 : HG[hr][3 * h + 2] & 0xFFFF;
+                const uint64_t g = ((uint64_t)hi << 32) | HG[hr][3 * h + (q & 1)];
+                const uint32_t ng = (HN[hr] >> (8 * q)) & 0xFF;
+                place_group(g, ng, p, sh.buf);
+                p += ng;
+            }
+        }
         __syncthreads();
         if (wave == 0) {
-            const uint64_t excl = lookback(ws + 1, s, words, lane);
+            const uint64_t excl = lookback(ws + 1, s, words, lane, kHold > 0);
             if (lane == 0) {
                 sh.misc[1] = (uint32_t)excl;
                 sh.misc[2] = (uint32_t)(excl >> 32);
