@@ -10,8 +10,9 @@
 // persistent and walk the groups with a stride of the grid size.  While a
 // workgroup decodes group k out of LDS, the loads of group k+1 (its
 // container entries, then its payload span into registers, two 16-byte
-// loads per lane after each of the steps 6-14 of the first 128 symbols) are
-// in flight, so HBM latency is hidden behind decoding.  Per group:
+// loads per lane after each of the steps 0-8 of the first 128 symbols; the
+// span's entries come one group earlier still) are in flight, so HBM
+// latency is hidden behind decoding.  Per group:
 //   1. the staged span sits in LDS in rows of 68 words: 64 payload words plus
 //      copies of the next row's first four, so any 4-word window read stays
 //      in one row, rows start 16-byte aligned, and lanes whose sub-streams
@@ -446,6 +447,9 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
     span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
     Prefetch pf;
     issue_prefetch(pf, pq, lo, last_quad(lo, hi, payload_words), tid0);
+    // the next group's span entries, one group ahead
+    SpanEntries nspan = load_span(grp + gridDim.x < num_full ? grp + gridDim.x : grp, num_sub, chunk, num_chunks,
+                                  cwo, sub_off);
     uint32_t o1[kHalfWords], o2[kHalfWords];
 
     for (;;) {
@@ -505,23 +509,21 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
         const bool more = nxt < num_full;
         const uint64_t nxt_c = more ? nxt : grp;
         const LaneMeta nmeta = load_meta(nxt_c * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
-        const SpanEntries nspan = load_span(nxt_c, num_sub, chunk, num_chunks, cwo, sub_off);
+        const uint64_t nn = nxt + gridDim.x;
+        const SpanEntries nspan2 = load_span(nn < num_full ? nn : nxt_c, num_sub, chunk, num_chunks, cwo, sub_off);
         uint64_t nlo = 0, nhi = 0, nq_lo = 0, nq_last = 0;
+        span_words(nspan, payload_words, nlo, nhi);
+        nq_last = more ? last_quad(nlo, nhi, payload_words) : 0;
+        nq_lo = more ? nlo : 0;
         const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
         uint8_t *dst = out + (grp * kThreads + tid) * kSub;
         const LdsWords src{stage, (uint32_t)((cnt < stage_cap ? cnt : stage_cap) - (cnt > 0 ? 1 : 0))};
         uint32_t bad = 0;
-        // first half: the next span's bounds after step 5, its payload loads
-        // two per step from step 6
+        // first half: the next group's payload loads, two per step from step
+        // 0 (its span entries were loaded one group ahead)
         uint32_t pos = decode_half<MODE, CHECK>(src, job.pos0, t, bad, o1, [&](uint32_t q) {
-            if (q == 5) {
-                span_words(nspan, payload_words, nlo, nhi);
-                // past the last group: one quad, read by every lane
-                nq_last = more ? last_quad(nlo, nhi, payload_words) : 0;
-                nq_lo = more ? nlo : 0;
-            }
-            if (q >= 6 && 2 * (q - 6) < kPrefetch) prefetch_quad(pf, 2 * (q - 6), pq, nq_lo, nq_last, tid);
-            if (q >= 6 && 2 * (q - 6) + 1 < kPrefetch) prefetch_quad(pf, 2 * (q - 6) + 1, pq, nq_lo, nq_last, tid);
+            if (2 * q < kPrefetch) prefetch_quad(pf, 2 * q, pq, nq_lo, nq_last, tid);
+            if (2 * q + 1 < kPrefetch) prefetch_quad(pf, 2 * q + 1, pq, nq_lo, nq_last, tid);
         });
         // second half: the first half's 128 bytes, 16 per step
         if (staged) store_half(dst, o1);
@@ -536,6 +538,7 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
         meta = nmeta;
         lo = nlo;
         hi = nhi;
+        nspan = nspan2;
     }
 }
 
