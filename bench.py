@@ -169,6 +169,16 @@ def cpu_baseline_leg(x_np, counts_prev, kind, qlc_bits, chunk, gpu_streams, targ
         "oracle_round_trip": bool(rc == 0 and np.array_equal(y, part)),
     }
     del spc
+    # one thread, on a smaller sample (about a second of work)
+    n1 = int(min(x_np.size, max(chunk, (rate / max(threads, 1)) * 1.0 // chunk * chunk)))
+    p1 = x_np[:n1]
+    t0 = time.perf_counter()
+    s1 = coder.encode(p1, book["lengths"], book["codes"], chunk, threads=1)
+    t1 = time.perf_counter()
+    coder.decode(s1, p1.size, chunk, book, threads=1)
+    t2 = time.perf_counter()
+    single = {"value": round(p1.size / (t2 - t0) / 1e9, 4), "bytes": int(p1.size),
+              "encode_GBps": round(p1.size / (t1 - t0) / 1e9, 4), "decode_GBps": round(p1.size / (t2 - t1) / 1e9, 4)}
     return {
         "value": round(part.size / (te + td) / 1e9, 4),
         "unit": "GB/s",
@@ -178,8 +188,19 @@ def cpu_baseline_leg(x_np, counts_prev, kind, qlc_bits, chunk, gpu_streams, targ
                   "decode %.2f s" % (nch, nchunks_total, part.size, te, td),
         "encode_GBps": round(part.size / te / 1e9, 4),
         "decode_GBps": round(part.size / td / 1e9, 4),
+        "single_thread": single,
         "cpu_model": _cpu_model(),
     }, parity
+
+
+def ms_stats(v):
+    """mean, median, p10, p90, min and max of per-call times (ms)."""
+    import numpy as np
+
+    a = np.asarray(v, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 4), "median": round(float(np.median(a)), 4),
+            "p10": round(float(np.percentile(a, 10)), 4), "p90": round(float(np.percentile(a, 90)), 4),
+            "min": round(float(a.min()), 4), "max": round(float(a.max()), 4)}
 
 
 def _cpu_model():
@@ -392,7 +413,9 @@ def main():
     traffic = load_traffic(dom)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
-                "algorithmic_bytes": alg[dom], "avg_ms": round(avg[dom], 4)}
+                "algorithmic_bytes": alg[dom], "avg_ms": round(avg[dom], 4),
+                # against what a plain device copy reaches on the same GPU
+                "frac_of_device_copy": round(achieved / copy_GBps, 4)}
     other = "decode" if dom == "encode" else "encode"
     other_ach = alg[other] / (avg[other] * 1e-3) / 1e9
 
@@ -435,11 +458,12 @@ def main():
                    "description": w.description},
         "encode_GBps": round(n / (avg["encode"] * 1e-3) / 1e9, 1),
         "decode_GBps": round(n / (avg["decode"] * 1e-3) / 1e9, 1),
-        "encode_ms": {"mean": round(avg["encode"], 4), "min": round(min(enc_ms), 4), "max": round(max(enc_ms), 4)},
-        "decode_ms": {"mean": round(avg["decode"], 4), "min": round(min(dec_ms), 4), "max": round(max(dec_ms), 4)},
+        "encode_ms": ms_stats(enc_ms),
+        "decode_ms": ms_stats(dec_ms),
         "roofline": roofline,
         "roofline_other": {"kernel": other, "achieved": round(other_ach, 1),
-                           "frac": round(other_ach / HBM_PEAK_GBPS, 4)},
+                           "frac": round(other_ach / HBM_PEAK_GBPS, 4),
+                           "frac_of_device_copy": round(other_ach / copy_GBps, 4)},
         "device_copy_GBps": round(copy_GBps, 1),
         "bits_per_symbol": {"payload": round(b_payload, 5), "with_side_index": round(b_total, 5),
                             "entropy": round(H, 5), "per_shard_huffman12": round(shard_bits, 5),
