@@ -33,6 +33,8 @@
 // compresses produces such groups).  The QLC variant replaces the 12-bit
 // table with the page's own decoder: a 3-bit area number, that area's
 // fixed-width index, and the 256-entry rank -> symbol table.
+#include <atomic>
+
 #include "pc_internal.h"
 
 namespace pc {
@@ -662,21 +664,28 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     // words (8 bits per symbol from a row-aligned start).
     const uint64_t cap = kStageRows * kRow;
     const size_t shmem = kStageRows * kRowPad * 4;
-    static bool attr_set[2] = {false, false};
-    static int num_cus = 0;
+    // Per device (the current one), set once: its CU count, and the
+    // dynamic-LDS limit of the main kernels.  Concurrent first calls may
+    // both query and set; they store the same values.
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cus_of[kMaxDevices];
+    static std::atomic<bool> attr_of[kMaxDevices][2];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int num_cus = cus_of[dev].load(std::memory_order_relaxed);
     if (!num_cus) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
+        e = hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
+        cus_of[dev].store(num_cus, std::memory_order_relaxed);
     }
     const void *fn = mode == kDecodeLut12 ? (const void *)decode_kernel<kDecodeLut12>
                                           : (const void *)decode_kernel<kDecodeQlc>;
-    if (!attr_set[mode]) {
-        const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 kStageRows * kRowPad * 4);
+    if (!attr_of[dev][mode].load(std::memory_order_relaxed)) {
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kStageRows * kRowPad * 4);
         if (e != hipSuccess) return e;
-        attr_set[mode] = true;
+        attr_of[dev][mode].store(true, std::memory_order_relaxed);
     }
     // groups whose 256 sub-streams all hold 256 symbols inside [0, n)
     // (the main kernel's prefetch needs one whole 16-byte quad of payload)
