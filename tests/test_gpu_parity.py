@@ -380,3 +380,41 @@ def test_histogram_matches_bincount():
             want = 2 * np.bincount(x.cpu().numpy(), minlength=256)
             assert np.array_equal(counts.cpu().numpy(), want)
     del rng
+
+
+# --------------------------------------------------------------------------
+# streams and buffer reuse
+# --------------------------------------------------------------------------
+
+def test_side_streams_and_reused_buffers():
+    """Two encode + decode pipelines on two non-default streams at once,
+    each with its own outputs and workspace, run twice with the buffers of
+    the first run reused (stale contents, including the look-back
+    workspace, must not matter)."""
+    dcb, obook = make_book(random_counts(31))
+    chunk = 65536
+    inputs = [skewed(5 * chunk + 300, 41), skewed(7 * chunk, 42)]
+    xs = [torch.from_numpy(a).to(DEV) for a in inputs]
+    outs = [pc.alloc_encode_outputs(a.size, chunk, torch.device(DEV)) for a in inputs]
+    dec_out = [torch.empty(a.size, dtype=torch.uint8, device=DEV) for a in inputs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    torch.cuda.synchronize()
+    for rep in range(2):
+        say("side streams: pass", rep)
+        encs, stats = [None, None], [None, None]
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                encs[i] = pc.pc_encode(dcb, xs[i], chunk, outputs=outs[i])
+                stats[i] = torch.zeros(1, dtype=torch.int32, device=DEV)
+                pc.pc_decode(dcb, encs[i], out=dec_out[i], status=stats[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            want = coder.encode(inputs[i], obook["lengths"], obook["codes"], chunk, threads=4)
+            assert_same_stream(host(encs[i]), want)
+            assert int(stats[i].item()) == 0
+            assert torch.equal(dec_out[i][:inputs[i].size], xs[i])
+        for i in range(2):  # stale contents for the second pass
+            outs[i][0].fill_(-1)
+            outs[i][4].fill_(-1)
+            dec_out[i].fill_(0)
+        torch.cuda.synchronize()
