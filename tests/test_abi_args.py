@@ -1,0 +1,68 @@
+"""Argument checks of the device entry points, on the CPU: every call here
+is rejected before the library touches the device (fake, never dereferenced
+addresses), so no GPU is needed."""
+import ctypes as C
+
+import pytest
+
+import static_codebook_lossless_amd as pc
+
+lib = pc._lib.lib
+P = C.c_void_p
+A = P(1 << 20)      # 16-byte aligned fake device address
+ODD = P((1 << 20) + 4)  # 4-byte aligned only
+CHUNK = 65536
+
+
+def enc(cb=A, x=A, n=1000, chunk=CHUNK, payload=A, cap=None, bits=A, cwo=A, sub=A, ws=A, ws_bytes=None):
+    cap = pc.pc_max_payload_words(n, chunk) if cap is None else cap
+    ws_bytes = pc.pc_encode_workspace_bytes(n, chunk) if ws_bytes is None else ws_bytes
+    return lib.pc_encode(cb, x, n, chunk, payload, cap, bits, cwo, sub, ws, ws_bytes, None)
+
+
+def dec(fn, cb=A, payload=A, words=100, bits=A, cwo=A, sub=A, n=1000, chunk=CHUNK, out=A, status=A):
+    return fn(cb, payload, words, bits, cwo, sub, n, chunk, out, status, None)
+
+
+@pytest.mark.parametrize("chunk", [0, 1, 255, 257, 1000, (1 << 24) + 256, 1 << 25])
+def test_bad_chunk_sizes(chunk):
+    assert enc(chunk=chunk, cap=1 << 30, ws_bytes=1 << 30) == pc.PC_ERR_INVALID_ARG
+    for fn in (lib.pc_decode, lib.pc_decode_qlc):
+        assert dec(fn, chunk=chunk) == pc.PC_ERR_INVALID_ARG
+    assert pc.pc_num_chunks(1000, chunk) == 0 and pc.pc_max_payload_words(1000, chunk) == 0
+    assert pc.pc_encode_workspace_bytes(1000, chunk) == 0
+
+
+@pytest.mark.parametrize("which", ["cb", "x", "payload", "bits", "cwo", "sub", "ws"])
+def test_encode_null_pointers(which):
+    assert enc(**{which: None}) == pc.PC_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which", ["cb", "x", "payload", "cwo", "ws"])
+def test_encode_misaligned_pointers(which):
+    assert enc(**{which: ODD}) == pc.PC_ERR_INVALID_ARG
+
+
+def test_encode_capacity():
+    assert enc(cap=pc.pc_max_payload_words(1000, CHUNK) - 1) == pc.PC_ERR_CAPACITY
+    assert enc(ws_bytes=pc.pc_encode_workspace_bytes(1000, CHUNK) - 1) == pc.PC_ERR_CAPACITY
+
+
+@pytest.mark.parametrize("which", ["cb", "payload", "bits", "cwo", "sub", "out", "status"])
+def test_decode_null_pointers(which):
+    for fn in (lib.pc_decode, lib.pc_decode_qlc):
+        assert dec(fn, **{which: None}) == pc.PC_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which", ["cb", "payload", "out"])
+def test_decode_misaligned_pointers(which):
+    for fn in (lib.pc_decode, lib.pc_decode_qlc):
+        assert dec(fn, **{which: ODD}) == pc.PC_ERR_INVALID_ARG
+
+
+def test_empty_decode_and_histogram_touch_nothing():
+    for fn in (lib.pc_decode, lib.pc_decode_qlc):
+        assert dec(fn, cb=None, payload=None, bits=None, cwo=None, sub=None, out=None, status=None, n=0) == pc.PC_OK
+    assert lib.pc_histogram(None, 0, None, None) == pc.PC_OK
+    assert lib.pc_histogram(None, 10, A, None) == pc.PC_ERR_INVALID_ARG
+    assert lib.pc_histogram(A, 10, ODD, None) == pc.PC_ERR_INVALID_ARG

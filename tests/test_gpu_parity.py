@@ -418,3 +418,13 @@ def test_side_streams_and_reused_buffers():
             outs[i][4].fill_(-1)
             dec_out[i].fill_(0)
         torch.cuda.synchronize()
+
+
+def test_largest_chunk_size():
+    """Chunks of 2^24 symbols (the largest the container allows): one full
+    chunk and a short one, and a single partial chunk."""
+    dcb, obook = make_book(random_counts(51))
+    chunk = 1 << 24
+    for n in (chunk + 12345, 3 * (1 << 20) + 7):
+        say("largest chunk:", chunk, "n", n)
+        roundtrip(dcb, obook, skewed(n, n % 1000), chunk)
