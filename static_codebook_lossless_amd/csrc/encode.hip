@@ -407,7 +407,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
         }
         __syncthreads();
         uint32_t *dst = payload + (((uint64_t)sh.misc[2] << 32) | sh.misc[1]);
-        for (uint32_t i = tid; i < words; i += THREADS) dst[i] = sh.buf[i];
+        // streaming stores: the payload is not read again here, and the
+        // workgroup's consecutive lanes cover whole lines
+        for (uint32_t i = tid; i < words; i += THREADS) __builtin_nontemporal_store(sh.buf[i], dst + i);
         return;
     }
 
