@@ -406,10 +406,14 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
             }
         }
         __syncthreads();
-        uint32_t *dst = payload + (((uint64_t)sh.misc[2] << 32) | sh.misc[1]);
-        // streaming stores: the payload is not read again here, and the
-        // workgroup's consecutive lanes cover whole lines
-        for (uint32_t i = tid; i < words; i += THREADS) __builtin_nontemporal_store(sh.buf[i], dst + i);
+        const uint64_t excl = ((uint64_t)sh.misc[2] << 32) | sh.misc[1];
+        uint32_t *dst = payload + excl;
+        // streaming stores (the payload is not read again here); after a
+        // head up to a 128-byte boundary every wave writes whole lines
+        const uint32_t head = (uint32_t)((32 - (excl & 31)) & 31) < words ? (uint32_t)((32 - (excl & 31)) & 31)
+                                                                          : (uint32_t)words;
+        if (tid < head) __builtin_nontemporal_store(sh.buf[tid], dst + tid);
+        for (uint32_t i = head + tid; i < words; i += THREADS) __builtin_nontemporal_store(sh.buf[i], dst + i);
         return;
     }
 
