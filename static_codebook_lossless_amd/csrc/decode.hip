@@ -32,7 +32,10 @@
 // that decodes it straight from global memory (only data that barely
 // compresses produces such groups).  The QLC variant replaces the 12-bit
 // table with the page's own decoder: a 3-bit area number, that area's
-// fixed-width index, and the 256-entry rank -> symbol table.
+// fixed-width index, and the 256-entry rank -> symbol table.  Its per-area
+// widths and first ranks sit in registers (looked up with v_perm), so the
+// decoding chain holds no memory read; only the rank -> symbol read, beside
+// the chain, goes to LDS.
 #include <atomic>
 
 #include "pc_internal.h"
@@ -83,16 +86,21 @@ struct GlobalWords {
 };
 
 struct Tables {
-    const uint16_t *lut;   // LDS: 4096 x ((19 - length) | symbol << 8), 0 = no codeword
-    const uint8_t *sym;    // LDS: sym_of_rank[256] (QLC mode)
-    const uint32_t *area;  // LDS: per area (index bits | first rank << 8) (QLC mode)
+    const uint16_t *lut;  // LDS: 4096 x ((19 - length) | symbol << 8), 0 = no codeword
+    const uint8_t *sym;   // LDS (QLC mode): symbol of rank r for r < 256, 0 up to 1023
+    // QLC mode, one byte per area a (a = 0..3 in *_lo, 4..7 in *_hi), read
+    // with v_perm, so that no table on the decoding chain sits in memory:
+    uint32_t sh_lo, sh_hi;  // 29 - b_a = 32 - codeword length
+    uint32_t bw_lo, bw_hi;  // b_a, bit 7 set when the area starts past rank 255
+    uint32_t st_lo, st_hi;  // first rank of the area (0 when past 255)
 };
 
 // Decode 8 symbols from the 96-bit window (h, m, l); returns them packed
 // little-endian in two words and adds the bits consumed to pos.  Symbols at
 // index >= lim (masked variant only) consume nothing.
 //
-// Entries (both modes) are (19 - length) | symbol << 8.  In LUT mode the
+// Entries are (19 - length) | symbol << 8 in LUT mode and (32 - length) |
+// symbol << 8 in QLC mode (formed in registers there).  In LUT mode the
 // byte offset of the next entry is taken from the window before it is
 // advanced: the 12 bits after a codeword of length len start len bits into
 // h, so (h >> (19 - len)) & 0x1FFE is twice their value, and v_lshrrev reads
@@ -109,39 +117,44 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
     uint32_t a = (h >> (31 - kPeek)) & 0x1FFE;  // byte offset of the first entry (LUT mode)
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        uint32_t ek, inv;
+        uint32_t ek, inv, sh;  // sh: 32 - length in the 5 bits v_alignbit reads
+        const bool masked = MASKED && k0 + k >= lim;  // length 0: the window is kept
         if (MODE == kDecodeLut12) {
             ek = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(t.lut) + a);
             inv = (ek & 0xFF) == 0;
+            if (masked) ek = (ek & 0xFF00) | 19;
+            if (k < 7) a = (h >> (ek & 31)) & 0x1FFE;
+            sh = ek + 13;
         } else {
-            const uint32_t ar = t.area[h >> 29];
-            const uint32_t b = ar & 15;
-            const uint32_t r = (ar >> 8) + __builtin_amdgcn_ubfe(h, 29 - b, b);
-            inv = r >= 256;
-            ek = (16 - b) | ((uint32_t)t.sym[r & 255] << 8);  // length 3 + b
+            // the area number (3 bits) selects bytes of the area registers
+            // (the other selector bytes, 0x0C, give zeros; one funnel shift
+            // forms the selector: (0x01818180 << 3) | (h >> 29)); the chain
+            // per symbol is funnel shift, v_perm, funnel shift, with the
+            // rank and the symbol read beside it
+            const uint32_t sel = __builtin_amdgcn_alignbit(0x01818180u, h, 29);
+            sh = __builtin_amdgcn_perm(t.sh_hi, t.sh_lo, sel);
+            const uint32_t bw = __builtin_amdgcn_perm(t.bw_hi, t.bw_lo, sel);
+            const uint32_t r = __builtin_amdgcn_perm(t.st_hi, t.st_lo, sel) + __builtin_amdgcn_ubfe(h, sh, bw);
+            inv = (bw >> 7) | (r >> 8);
+            ek = (masked ? 32u : sh) | ((uint32_t)t.sym[r] << 8);  // (32 - length) | symbol << 8
         }
-        if (MASKED && k0 + k >= lim) {
-            ek = (ek & 0xFF00) | 19;  // length 0; the window is kept below
-            inv = 0;
-        }
+        if (masked) inv = 0;
         if (CHECK) bad |= inv;
-        if (MODE == kDecodeLut12 && k < 7) a = (h >> (ek & 31)) & 0x1FFE;
-        const uint32_t sh = ek + 13;  // 32 - length in the 5 bits v_alignbit reads
         const uint32_t h2 = __builtin_amdgcn_alignbit(h, m, sh);
         const uint32_t m2 = __builtin_amdgcn_alignbit(m, l, sh);
         const uint32_t l2 = __builtin_amdgcn_alignbit(l, 0u, sh);
-        if (MASKED && (ek & 0xFF) == 19) {
-            // keep the window (a funnel shift by 32 would read as 0)
-        } else {
+        if (!masked) {  // (a funnel shift by 32 would read as 0)
             h = h2;
             m = m2;
             l = l2;
         }
         e[k] = ek;
     }
-    // each low byte is 19 - length: 4 of them sum below 256
+    // each low byte is 19 - length (LUT mode) or 32 - length (QLC mode): 4
+    // of them sum below 256
+    constexpr uint32_t kBias = MODE == kDecodeLut12 ? 19 : 32;
     const uint32_t s0 = (e[0] + e[1] + e[2] + e[3]) & 0xFF, s1 = (e[4] + e[5] + e[6] + e[7]) & 0xFF;
-    pos += 8 * 19 - s0 - s1;
+    pos += 8 * kBias - s0 - s1;
     o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
     o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
     // pack and check here: left to the scheduler, the packing sinks towards
@@ -378,7 +391,7 @@ __device__ __forceinline__ void issue_prefetch(Prefetch &pf, gquad *payload, uin
 
 // Tables into LDS (shared by both kernels).
 template <int MODE>
-__device__ __forceinline__ void load_tables(const uint8_t *cbb, uint4 *tab4, uint32_t *area_tab, uint32_t tid) {
+__device__ __forceinline__ void load_tables(const uint8_t *cbb, uint4 *tab4, uint32_t tid) {
     if (MODE == kDecodeLut12) {
         // 16-bit entries (19 - length) | symbol << 8 (0: no codeword)
         const uint8_t *ds = cbb + kOffDecSym, *dl = cbb + kOffDecSym + 4096;
@@ -388,14 +401,33 @@ __device__ __forceinline__ void load_tables(const uint8_t *cbb, uint4 *tab4, uin
             lut[i] = (uint16_t)(len ? ((19 - len) | ((uint32_t)ds[i] << 8)) : 0u);
         }
     } else {
-        if (tid < 64)
-            reinterpret_cast<uint32_t *>(tab4)[tid] = reinterpret_cast<const uint32_t *>(cbb + kOffSymOfRank)[tid];
-        if (tid < 8) {
-            const uint32_t b = cbb[kOffQlcBits + tid];
-            const uint32_t st = reinterpret_cast<const uint16_t *>(cbb + kOffQlcStart)[tid];
-            area_tab[tid] = b | (st << 8);
-        }
+        // symbol of rank r, then zeros up to rank 1023 (a rank is below
+        // 255 + 2^9 for any layout; ranks past 255 are no codeword)
+        for (uint32_t i = tid; i < 256; i += kThreads)
+            reinterpret_cast<uint32_t *>(tab4)[i] =
+                i < 64 ? reinterpret_cast<const uint32_t *>(cbb + kOffSymOfRank)[i] : 0u;
     }
+}
+
+// The QLC area registers (see Tables), from the blob's widths and starts.
+__device__ __forceinline__ void qlc_area_regs(const uint8_t *cbb, Tables &t) {
+    uint32_t sh[2] = {0, 0}, bw[2] = {0, 0}, st[2] = {0, 0};
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+        uint32_t b = cbb[kOffQlcBits + a];
+        b = b > PC_MAX_LEN - 3 ? PC_MAX_LEN - 3 : b;  // a valid blob has b <= 9
+        const uint32_t start = reinterpret_cast<const uint16_t *>(cbb + kOffQlcStart)[a];
+        const uint32_t j = a >> 2, sft = 8 * (a & 3);
+        sh[j] |= (29 - b) << sft;
+        bw[j] |= (b | (start > 255 ? 0x80u : 0u)) << sft;
+        st[j] |= (start > 255 ? 0u : start) << sft;
+    }
+    t.sh_lo = sh[0];
+    t.sh_hi = sh[1];
+    t.bw_lo = bw[0];
+    t.bw_hi = bw[1];
+    t.st_lo = st[0];
+    t.st_hi = st[1];
 }
 
 __device__ __forceinline__ bool span_staged(uint64_t lo, uint64_t hi, uint64_t payload_words, uint32_t stage_cap) {
@@ -558,19 +590,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status, uint32_t stage_cap) {
     // Tables at fixed LDS addresses (folded into the instructions' offset
     // fields); the payload staging rows are the dynamic part.
-    __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 16];
-    __shared__ uint32_t area_tab[8];
+    __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 64];
     extern __shared__ uint4 stage4[];
     uint32_t *stage = reinterpret_cast<uint32_t *>(stage4);
     const uint32_t tid = threadIdx.x;
     const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
     const pc_codebook *cbp = reinterpret_cast<const pc_codebook *>(cb);
-    load_tables<MODE>(cbb, tab4, area_tab, tid);
+    load_tables<MODE>(cbb, tab4, tid);
     const bool kind_ok = MODE == kDecodeLut12 || cbp->kind == PC_CODEBOOK_QLC;
     Tables t;
     t.lut = reinterpret_cast<const uint16_t *>(tab4);
     t.sym = reinterpret_cast<const uint8_t *>(tab4);
-    t.area = area_tab;
+    if (MODE == kDecodeQlc) qlc_area_regs(cbb, t);
 
     uint64_t grp = blockIdx.x;
     if (grp >= num_full) return;
@@ -599,8 +630,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     const uint32_t *__restrict__ sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub, uint64_t num_groups,
     uint64_t num_full, uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status,
     uint32_t stage_cap) {
-    __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 16];
-    __shared__ uint32_t area_tab[8];
+    __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 64];
     __shared__ uint32_t todo[kTestBatch];
     __shared__ uint32_t ntodo;
     const uint32_t tid = threadIdx.x;
@@ -611,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     Tables t;
     t.lut = reinterpret_cast<const uint16_t *>(tab4);
     t.sym = reinterpret_cast<const uint8_t *>(tab4);
-    t.area = area_tab;
+    if (MODE == kDecodeQlc) qlc_area_regs(cbb, t);
     const uint64_t G = gridDim.x;
     for (uint64_t base = blockIdx.x; base < num_groups; base += G * kTestBatch) {
         // this batch: groups base + l G, l = 0 .. 63
@@ -626,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
         __syncthreads();
         const uint32_t nt = ntodo;
         if (nt && !loaded) {
-            load_tables<MODE>(cbb, tab4, area_tab, tid);
+            load_tables<MODE>(cbb, tab4, tid);
             __syncthreads();
             loaded = true;
         }
