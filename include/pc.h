@@ -177,7 +177,8 @@ size_t pc_encode_workspace_bytes(size_t n, size_t chunk);
  *   d_ws, ws_bytes        scratch of at least pc_encode_workspace_bytes,
  *              8-byte aligned; its contents need no initialisation.
  * n = 0 writes chunk_word_offset[0] = 0 and nothing else.  Calls that share
- * a workspace must be ordered on one stream.
+ * a workspace must be ordered on one stream.  More than 2^31 - 1 chunks:
+ * PC_ERR_UNSUPPORTED.
  */
 pc_status pc_encode(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size_t chunk,
                     uint32_t *d_payload, size_t payload_capacity_words,
@@ -202,6 +203,8 @@ pc_status pc_encode(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size
  *              that is no codeword, or a sub-stream that does not end exactly
  *              where the next one starts / at chunk_bits).  On such an error
  *              d_out holds unspecified bytes.
+ * 2^32 - 256 or more sub-streams (n of about 2^40 and up, past one GPU's
+ * memory): PC_ERR_UNSUPPORTED.
  */
 pc_status pc_decode(const pc_codebook *d_cb, const uint32_t *d_payload, size_t payload_words,
                     const uint32_t *d_chunk_bits, const uint64_t *d_chunk_word_offset,

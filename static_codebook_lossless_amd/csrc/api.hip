@@ -23,8 +23,8 @@ pc_status check_decode_args(const pc_codebook *d_cb, const uint32_t *d_payload, 
     if (!aligned(d_cb, 16) || !aligned(d_payload, 16) || !aligned(d_out, 16) || !aligned(d_cwo, 8) ||
         !aligned(d_chunk_bits, 4) || !aligned(d_sub_off, 4) || !aligned(d_status, 4))
         return PC_ERR_INVALID_ARG;
-    if (pc_num_chunks(n, chunk) > 0xFFFFFFFFull || pc_num_substreams(n, chunk) / 256 >= 0x7FFFFFFFull)
-        return PC_ERR_UNSUPPORTED;
+    // sub-stream indices are 32-bit on the device (n below about 2^40)
+    if (pc_num_substreams(n, chunk) >= pc::kMaxDecodeSubstreams) return PC_ERR_UNSUPPORTED;
     return PC_OK;
 }
 

@@ -262,7 +262,7 @@ __device__ __forceinline__ LaneMeta load_meta(uint64_t g, uint64_t num_sub, uint
                                               const uint32_t *chunk_bits, const uint64_t *cwo,
                                               const uint32_t *sub_off) {
     const bool active = g < num_sub;
-    const uint32_t gc = (uint32_t)(active ? g : num_sub - 1);  // num_sub < 2^32 (checked by the launcher)
+    const uint32_t gc = (uint32_t)(active ? g : num_sub - 1);  // num_sub < 2^32 - 256 (checked by the entry point)
     const uint32_t spc = chunk / kSub;
     const uint32_t c = gc / spc;
     const uint32_t j = gc - c * spc;
@@ -724,7 +724,7 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     if (grid > num_full) grid = num_full;
     uint64_t grid_g = (uint64_t)num_cus * kGroupsPerCU;
     if (grid_g > num_groups) grid_g = num_groups;
-    if (num_sub >= 0xFFFFFFFFull) return hipErrorInvalidValue;
+    if (num_sub >= kMaxDecodeSubstreams) return hipErrorInvalidValue;  // the entry point checks first
 #define PC_DEC(K)                                                                                             \
     hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), shmem, stream, cb, payload, payload_words,     \
                        chunk_bits, cwo, sub_off, n, chunk, num_sub, num_full, nc, out, status, (uint32_t)cap)

@@ -13,6 +13,8 @@ constexpr uint32_t kWave = 64;
 constexpr uint32_t kSub = PC_SUBSTREAM;  // symbols per decode sub-stream
 constexpr uint32_t kPeek = PC_MAX_LEN;   // bits looked at per codeword
 constexpr size_t kMaxChunk = (size_t)1 << 24;
+// decode: sub-stream indices, and an index plus 256, stay below 2^32
+constexpr uint64_t kMaxDecodeSubstreams = 0xFFFFFF00ull;
 
 // Byte offsets inside pc_codebook (checked by static_asserts in codebook.cpp).
 constexpr uint32_t kOffLength = 32;

@@ -66,3 +66,13 @@ def test_empty_decode_and_histogram_touch_nothing():
     assert lib.pc_histogram(None, 0, None, None) == pc.PC_OK
     assert lib.pc_histogram(None, 10, A, None) == pc.PC_ERR_INVALID_ARG
     assert lib.pc_histogram(A, 10, ODD, None) == pc.PC_ERR_INVALID_ARG
+
+
+def test_size_limits():
+    # the largest sizes each entry point serves, checked before any device
+    # access: encode up to 2^31 - 1 chunks, decode below 2^32 - 256 sub-streams
+    big = 1 << 46
+    assert enc(n=big, chunk=256, cap=1 << 62, ws_bytes=1 << 62) == pc.PC_ERR_UNSUPPORTED
+    for fn in (lib.pc_decode, lib.pc_decode_qlc):
+        assert dec(fn, n=(0xFFFFFF00) * 256, chunk=1 << 24) == pc.PC_ERR_UNSUPPORTED
+        assert dec(fn, n=big) == pc.PC_ERR_UNSUPPORTED
