@@ -165,10 +165,11 @@ __device__ __forceinline__ void pack_lane(const uint4 &x, uint32_t valid, uint32
         const uint32_t p23 = (c2 << l3) | c3, n23 = l2 + l3;
         const uint64_t g = ((uint64_t)p01 << n23) | p23;
         const uint32_t ng = n01 + n23;
-        if (valid < 16 && ng == 0) continue;
         // left-align the group in 64 bits, then spread it over 3 words at
-        // bit offset o inside word wi
-        const uint64_t a = g << (64 - ng);
+        // bit offset o inside word wi; a lane with no bits (past the end)
+        // ORs zeros, in bounds, so every OR is issued by every lane (see
+        // place_group)
+        const uint64_t a = ng ? g << (64 - ng) : 0ull;
         const uint32_t hi = (uint32_t)(a >> 32), lo = (uint32_t)a;
         const uint32_t o = p & 31, wi = p >> 5;
         atomicOr(&sh.stage[wi], hi >> o);
