@@ -84,11 +84,11 @@ def pmc_summary(fetch_dir, write_dir, copy_bytes, out=TRAFFIC_FILE):
         res[counter] = {"scale": scale, "kernels": {k: sorted(v)[len(v) // 2] for k, v in per.items()}}
     lines = ["# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of bench.py.",
              "# Made by (from the repository root, after cd /tmp && export TMPDIR=/tmp):",
-             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o bench -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-secondary",
-             "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o bench -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-secondary",
-             "#   python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o bench -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-secondary" % fetch_dir,
+             "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o bench -- "
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-secondary" % write_dir,
+             "#   python3 bench.py --pmc-summary %s %s" % (fetch_dir, write_dir),
              "# Each counter is scaled by copy_bytes / counter(plain device copy of copy_bytes bytes).",
              "# Raw medians (KiB per dispatch): " + "; ".join(
                  "%s %s %.1f" % (c, lab, v / 1024.0)
