@@ -91,16 +91,29 @@ struct Tables {
     // QLC mode, one byte per area a (a = 0..3 in *_lo, 4..7 in *_hi), read
     // with v_perm, so that no table on the decoding chain sits in memory:
     uint32_t sh_lo, sh_hi;  // 29 - b_a = 32 - codeword length
-    uint32_t bw_lo, bw_hi;  // b_a, bit 7 set when the area starts past rank 255
+    uint32_t bw_lo, bw_hi;  // b_a
     uint32_t st_lo, st_hi;  // first rank of the area (0 when past 255)
+    // QLC codewords read as left-aligned 32-bit numbers (area number, then
+    // index) grow with the rank, so a window starts with a codeword of a
+    // rank below 256 exactly when it is below the left-aligned codeword of
+    // rank 256 -- when the areas have a slot for rank 256 at all
+    uint32_t qlc_lim;
+    bool qlc_check;
 };
+
+// Whether a sub-stream met a bit pattern that is no codeword: LUT mode ORs
+// the entries' invalid flags, QLC mode keeps the largest window seen.
+template <int MODE>
+__device__ __forceinline__ bool saw_invalid(uint32_t bad, const Tables &t) {
+    return MODE == kDecodeLut12 ? bad != 0 : (t.qlc_check && bad >= t.qlc_lim);
+}
 
 // Decode 8 symbols from the 96-bit window (h, m, l); returns them packed
 // little-endian in two words and adds the bits consumed to pos.  Symbols at
 // index >= lim (masked variant only) consume nothing.
 //
-// Entries are (19 - length) | symbol << 8 in LUT mode and (32 - length) |
-// symbol << 8 in QLC mode (formed in registers there).  In LUT mode the
+// Entries are (19 - length) | symbol << 8 in LUT mode; QLC mode keeps
+// 32 - length and the symbol in two registers.  In LUT mode the
 // byte offset of the next entry is taken from the window before it is
 // advanced: the 12 bits after a codeword of length len start len bits into
 // h, so (h >> (19 - len)) & 0x1FFE is twice their value, and v_lshrrev reads
@@ -113,7 +126,7 @@ struct Tables {
 template <int MODE, bool MASKED, bool CHECK>
 __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint32_t &pos, uint32_t &bad,
                                         const Tables &t, uint32_t k0, uint32_t lim, uint32_t &o0, uint32_t &o1) {
-    uint32_t e[8];
+    uint32_t e[8], y[8];  // y: the symbols (QLC mode)
     uint32_t a = (h >> (31 - kPeek)) & 0x1FFE;  // byte offset of the first entry (LUT mode)
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -130,16 +143,21 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
             // (the other selector bytes, 0x0C, give zeros; one funnel shift
             // forms the selector: (0x01818180 << 3) | (h >> 29)); the chain
             // per symbol is funnel shift, v_perm, funnel shift, with the
-            // rank and the symbol read beside it
+            // rank and the symbol read beside it (a rank past 255 reads a
+            // zero of the 1 KiB table)
             const uint32_t sel = __builtin_amdgcn_alignbit(0x01818180u, h, 29);
             sh = __builtin_amdgcn_perm(t.sh_hi, t.sh_lo, sel);
             const uint32_t bw = __builtin_amdgcn_perm(t.bw_hi, t.bw_lo, sel);
             const uint32_t r = __builtin_amdgcn_perm(t.st_hi, t.st_lo, sel) + __builtin_amdgcn_ubfe(h, sh, bw);
-            inv = (bw >> 7) | (r >> 8);
-            ek = (masked ? 32u : sh) | ((uint32_t)t.sym[r] << 8);  // (32 - length) | symbol << 8
+            if (CHECK && !masked) bad = bad > h ? bad : h;
+            ek = masked ? 32u : sh;
+            y[k] = t.sym[r];
+            inv = 0;
         }
-        if (masked) inv = 0;
-        if (CHECK) bad |= inv;
+        if (MODE == kDecodeLut12) {
+            if (masked) inv = 0;
+            if (CHECK) bad |= inv;
+        }
         const uint32_t h2 = __builtin_amdgcn_alignbit(h, m, sh);
         const uint32_t m2 = __builtin_amdgcn_alignbit(m, l, sh);
         const uint32_t l2 = __builtin_amdgcn_alignbit(l, 0u, sh);
@@ -150,13 +168,18 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
         }
         e[k] = ek;
     }
-    // each low byte is 19 - length (LUT mode) or 32 - length (QLC mode): 4
-    // of them sum below 256
-    constexpr uint32_t kBias = MODE == kDecodeLut12 ? 19 : 32;
-    const uint32_t s0 = (e[0] + e[1] + e[2] + e[3]) & 0xFF, s1 = (e[4] + e[5] + e[6] + e[7]) & 0xFF;
-    pos += 8 * kBias - s0 - s1;
-    o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
-    o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
+    if (MODE == kDecodeLut12) {
+        // each low byte is 19 - length: 4 of them sum below 256
+        const uint32_t s0 = (e[0] + e[1] + e[2] + e[3]) & 0xFF, s1 = (e[4] + e[5] + e[6] + e[7]) & 0xFF;
+        pos += 8 * 19 - s0 - s1;
+        o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
+        o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
+    } else {
+        // e[k] = 32 - length (<= 32 each)
+        pos += 8 * 32 - (e[0] + e[1] + e[2] + e[3]) - (e[4] + e[5] + e[6] + e[7]);
+        o0 = __builtin_amdgcn_perm(y[1], y[0], 0x0C0C0400u) | __builtin_amdgcn_perm(y[3], y[2], 0x04000C0Cu);
+        o1 = __builtin_amdgcn_perm(y[5], y[4], 0x0C0C0400u) | __builtin_amdgcn_perm(y[7], y[6], 0x04000C0Cu);
+    }
     // pack and check here: left to the scheduler, the packing sinks towards
     // the store and the checks towards the end of the stream, and both keep
     // all eight entries of every step alive until then
@@ -412,6 +435,8 @@ __device__ __forceinline__ void load_tables(const uint8_t *cbb, uint4 *tab4, uin
 // The QLC area registers (see Tables), from the blob's widths and starts.
 __device__ __forceinline__ void qlc_area_regs(const uint8_t *cbb, Tables &t) {
     uint32_t sh[2] = {0, 0}, bw[2] = {0, 0}, st[2] = {0, 0};
+    t.qlc_lim = 0;
+    t.qlc_check = false;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
         uint32_t b = cbb[kOffQlcBits + a];
@@ -419,8 +444,12 @@ __device__ __forceinline__ void qlc_area_regs(const uint8_t *cbb, Tables &t) {
         const uint32_t start = reinterpret_cast<const uint16_t *>(cbb + kOffQlcStart)[a];
         const uint32_t j = a >> 2, sft = 8 * (a & 3);
         sh[j] |= (29 - b) << sft;
-        bw[j] |= (b | (start > 255 ? 0x80u : 0u)) << sft;
+        bw[j] |= b << sft;
         st[j] |= (start > 255 ? 0u : start) << sft;
+        if (!t.qlc_check && start <= 256 && start + (1u << b) > 256) {  // the area of rank 256
+            t.qlc_lim = ((uint32_t)a << 29) | ((256 - start) << (29 - b));
+            t.qlc_check = true;
+        }
     }
     t.sh_lo = sh[0];
     t.sh_hi = sh[1];
@@ -563,7 +592,7 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
         if (staged) store_half(dst, o1);
         pos = decode_half<MODE, CHECK>(src, pos, t, bad, o2, [&](uint32_t q) {});
         if (staged) {
-            if (job.ok && (bad || pos != job.pos_want)) flag_corrupt(status);
+            if (job.ok && (saw_invalid<MODE>(bad, t) || pos != job.pos_want)) flag_corrupt(status);
             store_half(dst + kHalf, o2);
         }
 
@@ -673,7 +702,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
             uint32_t bad = 0;
             const uint32_t pos_end =
                 decode_masked<MODE>(src, job.pos0, job.lim, t, dst, bad, 0, kSub);
-            if (job.ok && (bad || pos_end != job.pos_want)) flag_corrupt(status);
+            if (job.ok && (saw_invalid<MODE>(bad, t) || pos_end != job.pos_want)) flag_corrupt(status);
         }
         __syncthreads();  // todo and ntodo are rewritten by the next batch
     }
