@@ -379,6 +379,13 @@ def test_histogram_matches_bincount():
             torch.cuda.synchronize()
             want = 2 * np.bincount(x.cpu().numpy(), minlength=256)
             assert np.array_equal(counts.cpu().numpy(), want)
+    # large enough that every workgroup loops: 4-load rounds, the single
+    # loads after them, and a ragged tail
+    big = torch.from_numpy(skewed(40_000_021, 11)).to(DEV)[3:]
+    say("histogram: offset 3 n", big.numel())
+    counts = pc.pc_histogram(big)
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(big.cpu().numpy(), minlength=256))
     del rng
 
 
