@@ -261,6 +261,31 @@ def test_qlc_equals_canonical_when_lengths_do_not_decrease():
         assert codes[order[r]] == canon[r]
 
 
+@pytest.mark.parametrize("bits", [(1, 3, 3, 3, 3, 5, 6, 7), (3, 3, 3, 3, 3, 4, 7, 7), (5, 4, 3, 3, 3, 3, 3, 8),
+                                  (0, 0, 1, 2, 4, 6, 7, 7), (8, 0, 0, 0, 0, 0, 0, 0)])
+def test_qlc_valid_windows_are_one_interval(bits):
+    # The QLC decoder's invalid-codeword test rests on this: read as
+    # left-aligned numbers, the windows that start with a codeword of the
+    # QLC code (ranks 0..255) are exactly those below the left-aligned
+    # codeword that rank 256 would get (none, when the areas hold exactly
+    # 256 ranks).  Checked by brute force over every 12-bit window, for
+    # layouts with growing, shrinking and empty areas.
+    lengths, codes, _, _ = cb.qlc_code(list(range(256, 0, -1)), bits)
+    valid = [False] * 4096
+    for s in range(256):
+        lo = codes[s] << (12 - lengths[s])
+        for p in range(lo, lo + (1 << (12 - lengths[s]))):
+            assert not valid[p]  # prefix-free
+            valid[p] = True
+    start, bound = 0, 4096
+    for a, b in enumerate(bits):
+        if start <= 256 < start + (1 << b):
+            bound = ((a << b) | (256 - start)) << (12 - 3 - b)
+            break
+        start += 1 << b
+    assert valid == [p < bound for p in range(4096)]
+
+
 def test_qlc_rejects_short_cover():
     with pytest.raises(ValueError):
         cb.qlc_code([1] * 256, (1, 1, 1, 1, 1, 1, 1, 1))
