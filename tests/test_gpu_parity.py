@@ -174,8 +174,11 @@ def test_edge_sizes(chunk):
 
 def test_group_boundaries():
     """Sizes around whole groups of 256 sub-streams (65536 symbols): full
-    groups and a ragged last group take different decode kernels."""
-    for kind, bits in (("huffman", None), ("qlc", (1, 3, 3, 3, 3, 5, 6, 7))):
+    groups and a ragged last group take different decode kernels.  QLC
+    layouts with shrinking and with empty areas move the codeword of rank
+    256, which bounds the QLC decoder's valid windows."""
+    for kind, bits in (("huffman", None), ("qlc", (1, 3, 3, 3, 3, 5, 6, 7)), ("qlc", (5, 4, 3, 3, 3, 3, 3, 8)),
+                       ("qlc", (0, 0, 1, 2, 4, 6, 7, 7))):
         dcb, obook = make_book(random_counts(21), kind, bits)
         for chunk in (4096, 65536):
             for n in (65535, 65536, 65537, 2 * 65536 - 256, 2 * 65536 + 255, 2 * 65536 + 256, 3 * 65536):
@@ -334,14 +337,15 @@ def test_corruptions_detected(kind):
             assert np.array_equal(out.cpu().numpy(), want)
 
 
-def test_unused_qlc_code_detected():
-    bits = (1, 3, 3, 3, 3, 5, 6, 7)
+@pytest.mark.parametrize("bits", [(1, 3, 3, 3, 3, 5, 6, 7), (5, 4, 3, 3, 3, 3, 3, 8)])
+def test_unused_qlc_code_detected(bits):
     counts = np.arange(256, 0, -1) * 10
     dcb, obook = make_book(counts, "qlc", bits)
     data = np.arange(256, dtype=np.uint8).repeat(4)  # byte r has rank r
     lengths, codes = list(obook["lengths"]), list(obook["codes"])
+    assert lengths[255] == 3 + bits[7]  # rank 255 lies in the last area
     codes_bad = codes[:]
-    codes_bad[255] = (7 << 7) | 127  # unused slot of the last area
+    codes_bad[255] = (7 << bits[7]) | ((1 << bits[7]) - 1)  # unused slot of the last area
     from tests_helpers import string_encode
     s = string_encode(list(data), lengths, codes_bad, 1024)
     enc = pc.Encoded(
