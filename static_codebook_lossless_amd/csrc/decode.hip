@@ -605,6 +605,63 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
     }
 }
 
+// The groups the main kernel leaves: those whose span exceeds the LDS
+// budget (the same span test picks them) and the last group when it is not
+// full.  Each lane reads its words straight from global memory and writes
+// only bytes below its symbol count.  Workgroup b owns the groups b, b + G,
+// b + 2G, ... (G workgroups); its first wave tests 64 of them at once (one
+// per lane), then the workgroup decodes the ones that were not staged, so
+// that a stream with no such group costs one round of entry loads, and a
+// stream of such groups is spread over all workgroups.
+constexpr uint32_t kTestBatch = 64;
+
+struct Leftovers {
+    uint32_t todo[kTestBatch];
+    uint32_t ntodo;
+};
+
+// Test the batch of groups base + l G, l = 0 .. 63: the ones for the
+// global-memory path go to lo.todo; returns their number (uniform).
+__device__ __forceinline__ uint32_t test_batch(Leftovers &lo_, uint64_t base, uint64_t G, uint64_t num_groups,
+                                               uint64_t num_full, uint64_t num_sub, uint32_t chunk,
+                                               uint64_t num_chunks, const uint64_t *cwo, const uint32_t *sub_off,
+                                               uint64_t payload_words, uint32_t stage_cap, uint32_t tid) {
+    if (tid == 0) lo_.ntodo = 0;
+    __syncthreads();
+    if (tid < kTestBatch && base + tid * G < num_groups) {
+        const uint64_t g = base + tid * G;
+        uint64_t lo, hi;
+        span_words_lane(load_span(g, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
+        if (g >= num_full || !span_staged(lo, hi, payload_words, stage_cap)) lo_.todo[atomicAdd(&lo_.ntodo, 1u)] = tid;
+    }
+    __syncthreads();
+    return uniform(lo_.ntodo);
+}
+
+// Decode the nt groups a test_batch of `base` listed (tables in LDS).
+template <int MODE>
+__device__ __forceinline__ void decode_batch(const Leftovers &lo_, uint32_t nt, uint64_t base, uint64_t G,
+                                             const Tables &t, bool kind_ok, const uint32_t *payload,
+                                             uint64_t payload_words, const uint32_t *chunk_bits,
+                                             const uint64_t *cwo, const uint32_t *sub_off, uint64_t n,
+                                             uint32_t chunk, uint64_t num_sub, uint64_t num_chunks, uint8_t *out,
+                                             uint32_t *status, uint32_t tid) {
+    for (uint32_t i = 0; i < nt; ++i) {
+        const uint64_t grp = base + lo_.todo[i] * G;
+        uint64_t lo, hi;
+        span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
+        const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
+        const LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
+        const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
+        if (payload_words <= wbase) continue;  // nothing readable: every lane was flagged
+        uint8_t *dst = out + (grp * kThreads + tid) * kSub;
+        GlobalWords src{payload + wbase, payload_words - wbase - 1};
+        uint32_t bad = 0;
+        const uint32_t pos_end = decode_masked<MODE>(src, job.pos0, job.lim, t, dst, bad, 0, kSub);
+        if (job.ok && (saw_invalid<MODE>(bad, t) || pos_end != job.pos_want)) flag_corrupt(status);
+    }
+}
+
 // Main kernel: the full groups (all 256 sub-streams of 256 symbols inside
 // [0, n)) whose span fits the staging rows, so no lane needs masking.  Each
 // half's 128 bytes per lane are stored as soon as they are decoded.  Lanes
@@ -616,10 +673,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
     const uint32_t *__restrict__ chunk_bits, const uint64_t *__restrict__ cwo,
     const uint32_t *__restrict__ sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub, uint64_t num_full,
-    uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status, uint32_t stage_cap) {
+    uint64_t num_chunks, uint64_t num_groups, uint8_t *__restrict__ out, uint32_t *__restrict__ status,
+    uint32_t stage_cap) {
     // Tables at fixed LDS addresses (folded into the instructions' offset
     // fields); the payload staging rows are the dynamic part.
     __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 64];
+    __shared__ Leftovers left;
     extern __shared__ uint4 stage4[];
     uint32_t *stage = reinterpret_cast<uint32_t *>(stage4);
     const uint32_t tid = threadIdx.x;
@@ -632,26 +691,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     t.sym = reinterpret_cast<const uint8_t *>(tab4);
     if (MODE == kDecodeQlc) qlc_area_regs(cbb, t);
 
-    uint64_t grp = blockIdx.x;
-    if (grp >= num_full) return;
-    if (cbp->complete == 1)
-        decode_groups<MODE, false>(grp, tid, t, kind_ok, stage, stage4, payload, payload_words, chunk_bits, cwo, sub_off,
-                                   n, chunk, num_sub, num_full, num_chunks, out, status, stage_cap);
-    else
-        decode_groups<MODE, true>(grp, tid, t, kind_ok, stage, stage4, payload, payload_words, chunk_bits, cwo, sub_off,
-                                  n, chunk, num_sub, num_full, num_chunks, out, status, stage_cap);
+    // this workgroup's first batch of leftover groups (see below), tested
+    // while the tables arrive; decoded after the staged groups
+    const uint64_t G = gridDim.x;
+    const uint32_t nt0 = test_batch(left, blockIdx.x, G, num_groups, num_full, num_sub, chunk, num_chunks, cwo,
+                                    sub_off, payload_words, stage_cap, tid);
+    const uint64_t grp = blockIdx.x;
+    if (grp < num_full) {
+        if (cbp->complete == 1)
+            decode_groups<MODE, false>(grp, tid, t, kind_ok, stage, stage4, payload, payload_words, chunk_bits, cwo,
+                                       sub_off, n, chunk, num_sub, num_full, num_chunks, out, status, stage_cap);
+        else
+            decode_groups<MODE, true>(grp, tid, t, kind_ok, stage, stage4, payload, payload_words, chunk_bits, cwo,
+                                      sub_off, n, chunk, num_sub, num_full, num_chunks, out, status, stage_cap);
+    }
+    __syncthreads();  // the tables are in LDS
+    decode_batch<MODE>(left, nt0, blockIdx.x, G, t, kind_ok, payload, payload_words, chunk_bits, cwo, sub_off, n,
+                       chunk, num_sub, num_chunks, out, status, tid);
+    for (uint64_t base = blockIdx.x + G * kTestBatch; base < num_groups; base += G * kTestBatch) {
+        __syncthreads();  // the previous batch's list is read
+        const uint32_t nt = test_batch(left, base, G, num_groups, num_full, num_sub, chunk, num_chunks, cwo, sub_off,
+                                       payload_words, stage_cap, tid);
+        decode_batch<MODE>(left, nt, base, G, t, kind_ok, payload, payload_words, chunk_bits, cwo, sub_off, n, chunk,
+                           num_sub, num_chunks, out, status, tid);
+    }
 }
 
-// The groups the main kernel leaves: those whose span exceeds the LDS
-// budget (the same span test picks them) and the last group when it is not
-// full.  Each lane reads its words straight from global memory and writes
-// only bytes below its symbol count.  Workgroup b owns the groups b, b + G,
-// b + 2G, ... (G workgroups); its first wave tests 64 of them at once (one
-// per lane), then the workgroup decodes the ones that were not staged, so
-// that a stream with no such group costs one round of entry loads, and a
-// stream of such groups is spread over all workgroups.
-constexpr uint32_t kTestBatch = 64;
-
+// Leftover groups alone, for inputs without a full group (no main kernel).
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
@@ -660,8 +726,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     uint64_t num_full, uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status,
     uint32_t stage_cap) {
     __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 64];
-    __shared__ uint32_t todo[kTestBatch];
-    __shared__ uint32_t ntodo;
+    __shared__ Leftovers left;
     const uint32_t tid = threadIdx.x;
     const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
     const pc_codebook *cbp = reinterpret_cast<const pc_codebook *>(cb);
@@ -673,38 +738,16 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     if (MODE == kDecodeQlc) qlc_area_regs(cbb, t);
     const uint64_t G = gridDim.x;
     for (uint64_t base = blockIdx.x; base < num_groups; base += G * kTestBatch) {
-        // this batch: groups base + l G, l = 0 .. 63
-        if (tid == 0) ntodo = 0;
-        __syncthreads();
-        if (tid < kTestBatch && base + tid * G < num_groups) {
-            const uint64_t g = base + tid * G;
-            uint64_t lo, hi;
-            span_words_lane(load_span(g, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
-            if (g >= num_full || !span_staged(lo, hi, payload_words, stage_cap)) todo[atomicAdd(&ntodo, 1u)] = tid;
-        }
-        __syncthreads();
-        const uint32_t nt = ntodo;
+        const uint32_t nt = test_batch(left, base, G, num_groups, num_full, num_sub, chunk, num_chunks, cwo, sub_off,
+                                       payload_words, stage_cap, tid);
         if (nt && !loaded) {
             load_tables<MODE>(cbb, tab4, tid);
             __syncthreads();
             loaded = true;
         }
-        for (uint32_t i = 0; i < nt; ++i) {
-            const uint64_t grp = base + todo[i] * G;
-            uint64_t lo, hi;
-            span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
-            const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
-            const LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
-            const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
-            if (payload_words <= wbase) continue;  // nothing readable: every lane was flagged
-            uint8_t *dst = out + (grp * kThreads + tid) * kSub;
-            GlobalWords src{payload + wbase, payload_words - wbase - 1};
-            uint32_t bad = 0;
-            const uint32_t pos_end =
-                decode_masked<MODE>(src, job.pos0, job.lim, t, dst, bad, 0, kSub);
-            if (job.ok && (saw_invalid<MODE>(bad, t) || pos_end != job.pos_want)) flag_corrupt(status);
-        }
-        __syncthreads();  // todo and ntodo are rewritten by the next batch
+        decode_batch<MODE>(left, nt, base, G, t, kind_ok, payload, payload_words, chunk_bits, cwo, sub_off, n, chunk,
+                           num_sub, num_chunks, out, status, tid);
+        __syncthreads();  // the list is rewritten by the next batch
     }
 }
 
@@ -756,17 +799,20 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     if (num_sub >= kMaxDecodeSubstreams) return hipErrorInvalidValue;  // the entry point checks first
 #define PC_DEC(K)                                                                                             \
     hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), shmem, stream, cb, payload, payload_words,     \
-                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_full, nc, out, status, (uint32_t)cap)
+                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_full, nc, num_groups, out, status,    \
+                       (uint32_t)cap)
 #define PC_DEC_G(K)                                                                                           \
     hipLaunchKernelGGL(K, dim3((uint32_t)grid_g), dim3(kThreads), 0, stream, cb, payload, payload_words,       \
                        chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, num_full, nc, out, status,    \
                        (uint32_t)cap)
+    // with a full group the main kernel also takes the leftover groups;
+    // without one, only the leftover kernel runs
     if (mode == kDecodeLut12) {
         if (grid) PC_DEC(decode_kernel<kDecodeLut12>);
-        PC_DEC_G(decode_global_kernel<kDecodeLut12>);
+        else PC_DEC_G(decode_global_kernel<kDecodeLut12>);
     } else {
         if (grid) PC_DEC(decode_kernel<kDecodeQlc>);
-        PC_DEC_G(decode_global_kernel<kDecodeQlc>);
+        else PC_DEC_G(decode_global_kernel<kDecodeQlc>);
     }
 #undef PC_DEC
 #undef PC_DEC_G
