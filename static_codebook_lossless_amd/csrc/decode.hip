@@ -28,9 +28,10 @@
 //      stores (whole 128-byte lines);
 //   4. the sub-stream must end exactly at the next sub-stream's first bit (or
 //      at chunk_bits); any mismatch sets *status = PC_ERR_CORRUPT.
-// A group whose span does not fit the LDS budget is left to a second kernel
-// that decodes it straight from global memory (only data that barely
-// compresses produces such groups).  The QLC variant replaces the 12-bit
+// A group whose span does not fit the LDS budget, and a last group that is
+// not full, are leftovers: after its staged groups, each workgroup decodes
+// its share of them straight from global memory (only data that barely
+// compresses produces unstaged groups).  The QLC variant replaces the 12-bit
 // table with the page's own decoder: a 3-bit area number, that area's
 // fixed-width index, and the 256-entry rank -> symbol table.  Its per-area
 // widths and first ranks sit in registers (looked up with v_perm), so the
@@ -187,7 +188,7 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
     if (CHECK) asm volatile("" : "+v"(bad));
 }
 
-// Masked decode (the second kernel): symbols [s_begin, s_end) of one
+// Masked decode (the leftover groups): symbols [s_begin, s_end) of one
 // sub-stream in blocks of 16; a lane writes only its bytes below lim (lanes
 // past the end of the stream own none).
 template <int MODE, class Src>
@@ -494,7 +495,7 @@ __device__ __forceinline__ LaneJob lane_job(LaneMeta m, bool kind_ok, uint64_t p
 // The group loop of a workgroup (CHECK: test every table entry for "no
 // codeword", needed only when the code is incomplete).  Every lane decodes
 // on every pass; a group whose span is not staged decodes stale rows and
-// stores nothing (the second kernel decodes it).
+// stores nothing (it is decoded later as a leftover).
 template <int MODE, bool CHECK>
 __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const Tables &t, bool kind_ok,
                                               uint32_t *stage, uint4 *stage4, const uint32_t *payload,
@@ -663,7 +664,8 @@ __device__ __forceinline__ void decode_batch(const Leftovers &lo_, uint32_t nt, 
 }
 
 // Main kernel: the full groups (all 256 sub-streams of 256 symbols inside
-// [0, n)) whose span fits the staging rows, so no lane needs masking.  Each
+// [0, n)) whose span fits the staging rows, so no lane needs masking, then
+// the workgroup's leftover groups.  Each
 // half's 128 bytes per lane are stored as soon as they are decoded.  Lanes
 // of a corrupt sub-stream decode from the start of the staged span (LDS
 // reads are clamped) and write unspecified bytes into their own 256-byte
