@@ -256,6 +256,25 @@ def test_incompressible_data(chunk):
     roundtrip(dcb, obook, x_np, chunk)
 
 
+
+def test_staged_and_leftover_groups_mixed():
+    """Many groups, every third one too large to stage: segments of 65536
+    bytes alternate between data the code fits and uniform random bytes it
+    codes at more than 8 bits per symbol.  Workgroups then meet unstaged
+    groups in the middle of their persistent loop and decode them, with the
+    ragged last group, after their staged ones."""
+    counts = np.bincount(skewed(1 << 20, 41), minlength=256).astype(np.int64)
+    dcb, obook = make_book(counts, "huffman", None)
+    rng = np.random.default_rng(43)
+    segs = []
+    for i in range(1100):
+        segs.append(rng.integers(0, 256, 65536, dtype=np.uint8) if i % 3 == 2 else skewed(65536, 1000 + i))
+    x_np = np.concatenate(segs + [skewed(777, 7)])
+    say("staged and leftover groups: n", x_np.size)
+    enc = roundtrip(dcb, obook, x_np, 65536)
+    bits = host(enc)["chunk_bits"].astype(np.int64)
+    assert (bits[2:1100:3] > 8 * 65536).all() and (bits[0:1100:3] < 8 * 65536).all()
+
 # --------------------------------------------------------------------------
 # corruption: the decoder's status must agree with the oracle decoder's and
 # nothing outside [0, n) may be written
