@@ -255,6 +255,8 @@ def qlc_leg(pc, W, dev):
     st = torch.zeros(1, dtype=torch.int32, device=dev)
     enc_ms = time_calls(lambda: pc.pc_encode(dq, x, w.chunk, outs), 10)
     enc = pc.pc_encode(dq, x, w.chunk, outs)
+    torch.cuda.synchronize()
+    enc_ok = int(enc.status.item()) == 0
     dec_ms = time_calls(lambda: pc.pc_decode(dq, enc, out=out, status=st), 10)
     ok_lut = int(st.item()) == 0 and bool(torch.equal(out, x))
     st.zero_()
@@ -263,7 +265,7 @@ def qlc_leg(pc, W, dev):
     xc = pc.pc_histogram(x).cpu().numpy().astype(np.float64)
     lq = pc.codebook_fields(book_q)["length"].astype(np.float64)
     lh = pc.codebook_fields(book_h)["length"].astype(np.float64)
-    ls = pc.codebook_fields(pc.pc_codebook_build(xc.astype(np.uint64), "huffman"))["length"].astype(np.float64)
+    ls = pc.pc_shard_code_lengths(xc.astype(np.uint64)).astype(np.float64)
     p = xc[xc > 0] / n
     H = float(-(p * np.log2(p)).sum())
     bq, bh, bs = (float((xc * l).sum()) / n for l in (lq, lh, ls))
@@ -271,7 +273,7 @@ def qlc_leg(pc, W, dev):
             "encode_GBps": round(n / (enc_ms * 1e-3) / 1e9, 1),
             "decode_lut12_GBps": round(n / (dec_ms * 1e-3) / 1e9, 1),
             "decode_qlc_GBps": round(n / (qdec_ms * 1e-3) / 1e9, 1),
-            "round_trip_ok": bool(ok_lut and ok_qlc),
+            "round_trip_ok": bool(enc_ok and ok_lut and ok_qlc),
             "bits_per_symbol": {"qlc": round(bq, 5), "huffman12_same_counts": round(bh, 5),
                                 "huffman12_own_counts": round(bs, 5), "entropy": round(H, 5),
                                 "qlc_compressibility": round(1 - bq / 8, 5),
@@ -385,9 +387,10 @@ def main():
 
     # ---- checks and stream statistics ---------------------------------
     st = int(status.item())
+    est = int(enc.status.item())
     same = bool(torch.equal(dec_out, x))
-    if st != 0 or not same:
-        log("ROUND TRIP FAILED: status %d, equal %s" % (st, same))
+    if st != 0 or est != 0 or not same:
+        log("ROUND TRIP FAILED: encode status %d, decode status %d, equal %s" % (est, st, same))
     nc = pc.pc_num_chunks(n, chunk)
     nsub = pc.pc_num_substreams(n, chunk)
     cbits = enc.chunk_bits.cpu().numpy().view(np.uint32).astype(np.int64)
@@ -397,8 +400,9 @@ def main():
     xcounts = pc.pc_histogram(x).cpu().numpy().astype(np.float64)
     p = xcounts[xcounts > 0] / n
     H = float(-(p * np.log2(p)).sum())
-    shard_blob = pc.pc_codebook_build(xcounts.astype(np.uint64), "huffman")
-    shard_len = pc.codebook_fields(shard_blob)["length"].astype(np.float64)
+    # per-shard comparator: a 12-bit Huffman code on the stream's own counts,
+    # absent byte values excluded
+    shard_len = pc.pc_shard_code_lengths(xcounts.astype(np.uint64)).astype(np.float64)
     shard_bits = float((xcounts * shard_len).sum()) / n
     b_payload = payload_bits / n
     b_total = (words * 32 + 32 * nsub + 96 * nc) / n
@@ -472,13 +476,13 @@ def main():
                             "compressibility": round(1 - b_payload / 8, 5),
                             "entropy_compressibility": round(1 - H / 8, 5)},
         "codebook_id": "%08x" % fields["codebook_id"],
-        "round_trip_ok": bool(st == 0 and same),
+        "round_trip_ok": bool(st == 0 and est == 0 and same),
         "cpu_baseline": cpu,
         "oracle_parity_sample": parity,
         "secondary": secondary,
     }
     print(json.dumps(res), flush=True)
-    return 0 if (st == 0 and same and (parity is None or all(v for k, v in parity.items() if k != "chunks"))) else 1
+    return 0 if (st == 0 and est == 0 and same and (parity is None or all(v for k, v in parity.items() if k != "chunks"))) else 1
 
 
 if __name__ == "__main__":

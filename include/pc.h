@@ -66,7 +66,8 @@ typedef enum pc_status {
     PC_ERR_UNSUPPORTED = 2, /* valid request this build cannot serve */
     PC_ERR_CAPACITY = 3,    /* an output or workspace buffer is too small */
     PC_ERR_CORRUPT = 4,     /* data do not form a valid container (decode) */
-    PC_ERR_HIP = 5          /* the HIP runtime reported an error */
+    PC_ERR_HIP = 5,         /* the HIP runtime reported an error */
+    PC_ERR_TIMEOUT = 6      /* a bounded device wait gave up (encode); outputs invalid */
 } pc_status;
 
 typedef enum pc_codebook_kind {
@@ -156,6 +157,22 @@ pc_status pc_qlc_optimal_bits(const uint64_t counts[256], uint8_t bits_out[8]);
  */
 pc_status pc_codebook_fit(const pc_codebook *cb, const uint64_t counts[256], double *avg_bits, double *entropy);
 
+/*
+ * Code lengths of the per-shard comparator (host, pure).  "Single-Stage
+ * Huffman Encoder for ML Compression" (abstract) measures the fixed codebook
+ * against Huffman codes built for each shard from its own statistics (the
+ * three-stage scheme: count, build, send the codebook).  This returns that
+ * code for one shard's histogram: package-merge limited to 12 bits over the
+ * byte values that occur (count > 0), with the same tie rules as
+ * pc_codebook_build; an absent byte value gets length 0 (no codeword), a
+ * histogram with one byte value gives it length 1, an all-zero histogram
+ * gives all zeros.  Unlike pc_codebook_build, counts are not floored: a
+ * shard's own code never has to code a byte it does not contain.
+ *   lengths_out[256]   written in full on PC_OK.
+ * PC_ERR_INVALID_ARG for NULL pointers.
+ */
+pc_status pc_shard_code_lengths(const uint64_t counts[256], uint8_t lengths_out[256]);
+
 /* Size queries (host, pure).  chunk must be a valid chunk size, else 0. */
 size_t pc_num_chunks(size_t n, size_t chunk);          /* ceil(n / chunk) */
 size_t pc_num_substreams(size_t n, size_t chunk);      /* sum over chunks of ceil(len_c / 256) */
@@ -163,7 +180,12 @@ size_t pc_max_payload_words(size_t n, size_t chunk);   /* sum over chunks of cei
 size_t pc_encode_workspace_bytes(size_t n, size_t chunk);
 
 /*
- * Encode n symbols (device, asynchronous on `stream`).
+ * Encode n symbols (device, asynchronous on `stream`): every byte becomes
+ * its codeword from the fixed codebook and the codewords are concatenated
+ * ("Single-Stage Huffman Encoder for ML Compression", abstract: symbol to
+ * codeword mapping with one precomputed codebook; "Quad Length Codes for
+ * Lossless Compression of e4m3", abstract, for the QLC codewords), chunk by
+ * chunk into the container described above.
  *   d_cb       device copy of a pc_codebook.
  *   d_in       n input bytes, 16-byte aligned.
  *   chunk      symbols per chunk: multiple of 256, 256 <= chunk <= 2^24.
@@ -176,14 +198,34 @@ size_t pc_encode_workspace_bytes(size_t n, size_t chunk);
  *   d_sub_off             [pc_num_substreams(n, chunk)] u32
  *   d_ws, ws_bytes        scratch of at least pc_encode_workspace_bytes,
  *              8-byte aligned; its contents need no initialisation.
- * n = 0 writes chunk_word_offset[0] = 0 and nothing else.  Calls that share
- * a workspace must be ordered on one stream.  More than 2^31 - 1 chunks:
- * PC_ERR_UNSUPPORTED.
+ *   d_status   one u32 in device memory (4-byte aligned).  The call first
+ *              sets it to 0 on the stream, then to PC_ERR_TIMEOUT if the
+ *              cross-chunk scan gave up waiting for an earlier workgroup's
+ *              word count (see pc_encode_set_wait_limit); the outputs are
+ *              then invalid.  Read it after the stream has executed the call.
+ * n = 0 writes chunk_word_offset[0] = 0, *d_status = 0 and nothing else.
+ * Calls that share a workspace must be ordered on one stream.  More than
+ * 2^31 - 1 chunks: PC_ERR_UNSUPPORTED.
  */
 pc_status pc_encode(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size_t chunk,
                     uint32_t *d_payload, size_t payload_capacity_words,
                     uint32_t *d_chunk_bits, uint64_t *d_chunk_word_offset, uint32_t *d_sub_off,
-                    void *d_ws, size_t ws_bytes, void *stream);
+                    void *d_ws, size_t ws_bytes, uint32_t *d_status, void *stream);
+
+/*
+ * Bound of the encoder's one device-side wait (host, process-wide; returns
+ * the previous bound).  The pages describe no GPU encoder; this library's
+ * chunks learn their output offsets from a single-pass scan in which a
+ * workgroup waits until the workgroups of all earlier chunks have published
+ * their word counts.  Every wave of that wait polls at most `polls` times,
+ * then gives up and reports PC_ERR_TIMEOUT through pc_encode's d_status
+ * instead of waiting on.  The default (polls = 0 restores it) is 2^20 polls,
+ * about a second: far beyond a correct run's wait, short enough that a
+ * workgroup held up by other work on a time-sliced GPU ends in an error
+ * rather than a hang.  Small limits make give-ups frequent (the tests use 1
+ * to exercise the report); each call reads the bound when it is made.
+ */
+uint32_t pc_encode_set_wait_limit(uint32_t polls);
 
 /*
  * Decode n symbols (device, asynchronous on `stream`) with the generic

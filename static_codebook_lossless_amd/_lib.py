@@ -17,15 +17,16 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpc.so")
 
-PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED, PC_ERR_CAPACITY, PC_ERR_CORRUPT, PC_ERR_HIP = range(6)
+PC_OK, PC_ERR_INVALID_ARG, PC_ERR_UNSUPPORTED, PC_ERR_CAPACITY, PC_ERR_CORRUPT, PC_ERR_HIP, PC_ERR_TIMEOUT = range(7)
 PC_CODEBOOK_HUFFMAN, PC_CODEBOOK_QLC = 0, 1
 CODEBOOK_BYTES = 9536
 SUBSTREAM = 256
 
 EXPORTS = [
     "pc_status_string", "pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits", "pc_codebook_fit",
+    "pc_shard_code_lengths",
     "pc_num_chunks", "pc_num_substreams", "pc_max_payload_words", "pc_encode_workspace_bytes",
-    "pc_encode", "pc_decode", "pc_decode_qlc", "pc_histogram",
+    "pc_encode", "pc_encode_set_wait_limit", "pc_decode", "pc_decode_qlc", "pc_histogram",
 ]
 
 
@@ -47,14 +48,18 @@ def _load():
     lib.pc_codebook_validate.argtypes = [p]
     lib.pc_qlc_optimal_bits.argtypes = [p, p]
     lib.pc_codebook_fit.argtypes = [p, p, p, p]
+    lib.pc_shard_code_lengths.argtypes = [p, p]
     for f in ("pc_num_chunks", "pc_num_substreams", "pc_max_payload_words", "pc_encode_workspace_bytes"):
         getattr(lib, f).argtypes = [sz, sz]
         getattr(lib, f).restype = sz
-    lib.pc_encode.argtypes = [p, p, sz, sz, p, sz, p, p, p, p, sz, p]
+    lib.pc_encode.argtypes = [p, p, sz, sz, p, sz, p, p, p, p, sz, p, p]
+    lib.pc_encode_set_wait_limit.argtypes = [C.c_uint32]
+    lib.pc_encode_set_wait_limit.restype = C.c_uint32
     lib.pc_decode.argtypes = [p, p, sz, p, p, p, sz, sz, p, p, p]
     lib.pc_decode_qlc.argtypes = [p, p, sz, p, p, p, sz, sz, p, p, p]
     lib.pc_histogram.argtypes = [p, sz, p, p]
-    for f in ("pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits", "pc_codebook_fit", "pc_encode",
+    for f in ("pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits", "pc_codebook_fit",
+              "pc_shard_code_lengths", "pc_encode",
               "pc_decode", "pc_decode_qlc", "pc_histogram"):
         getattr(lib, f).restype = i
     return lib
@@ -132,6 +137,15 @@ def pc_codebook_fit(cb: torch.Tensor, counts) -> tuple:
     return avg.value, ent.value
 
 
+def pc_shard_code_lengths(counts) -> np.ndarray:
+    """Lengths (uint8 [256], 0 = no codeword) of the per-shard comparator code
+    built on ``counts`` alone, absent byte values excluded."""
+    cnt = _counts_u64(counts)
+    out = np.zeros(256, dtype=np.uint8)
+    _check(lib.pc_shard_code_lengths(_ptr(cnt), _ptr(out)), "pc_shard_code_lengths")
+    return out
+
+
 def pc_num_chunks(n, chunk):
     return int(lib.pc_num_chunks(n, chunk))
 
@@ -173,33 +187,43 @@ class Encoded(NamedTuple):
     sub_off: torch.Tensor            # int32 [num_substreams]
     n: int
     chunk: int
+    status: torch.Tensor | None = None  # int32 [1]: PC_OK, or PC_ERR_TIMEOUT (outputs invalid)
 
 
 def alloc_encode_outputs(n, chunk, device):
+    """(payload, chunk_bits, chunk_word_offset, sub_off, workspace, status) device buffers."""
     nc = pc_num_chunks(n, chunk)
     payload = torch.empty(max(pc_max_payload_words(n, chunk), 4), dtype=torch.int32, device=device)
     chunk_bits = torch.empty(max(nc, 1), dtype=torch.int32, device=device)
     cwo = torch.empty(nc + 1, dtype=torch.int64, device=device)
     sub_off = torch.empty(max(pc_num_substreams(n, chunk), 1), dtype=torch.int32, device=device)
     ws = torch.empty(max(pc_encode_workspace_bytes(n, chunk) // 8, 1), dtype=torch.int64, device=device)
-    return payload, chunk_bits, cwo, sub_off, ws
+    status = torch.empty(1, dtype=torch.int32, device=device)
+    return payload, chunk_bits, cwo, sub_off, ws, status
+
+
+def pc_encode_set_wait_limit(polls: int) -> int:
+    """Set the encoder's bounded-wait limit (polls; 0 = the default); returns the previous one."""
+    return int(lib.pc_encode_set_wait_limit(int(polls)))
 
 
 def pc_encode(d_cb: torch.Tensor, d_in: torch.Tensor, chunk: int, outputs=None) -> Encoded:
     """Encode the uint8 device tensor ``d_in``.  ``outputs`` (from
     ``alloc_encode_outputs``) may be passed to reuse buffers.  Asynchronous
     on the current stream; ``payload`` is the full-capacity buffer, its first
-    ``chunk_word_offset[-1]`` words are the stream."""
+    ``chunk_word_offset[-1]`` words are the stream.  ``status`` (device) reads
+    PC_OK after the stream has run the call, unless the device-side wait gave
+    up (PC_ERR_TIMEOUT: the outputs are then invalid)."""
     if d_in.dtype != torch.uint8 or not d_in.is_cuda:
         raise TypeError("d_in must be a uint8 CUDA tensor")
     x = d_in.reshape(-1)
     n = x.numel()
-    payload, chunk_bits, cwo, sub_off, ws = outputs or alloc_encode_outputs(n, chunk, x.device)
+    payload, chunk_bits, cwo, sub_off, ws, status = outputs or alloc_encode_outputs(n, chunk, x.device)
     st = lib.pc_encode(_ptr(d_cb), _ptr(x), n, chunk, _ptr(payload), payload.numel(), _ptr(chunk_bits),
-                       _ptr(cwo), _ptr(sub_off), _ptr(ws), ws.numel() * 8, _stream(x.device))
+                       _ptr(cwo), _ptr(sub_off), _ptr(ws), ws.numel() * 8, _ptr(status), _stream(x.device))
     _check(st, "pc_encode")
     nc = pc_num_chunks(n, chunk)
-    return Encoded(payload, chunk_bits[:nc], cwo, sub_off[:pc_num_substreams(n, chunk)], n, chunk)
+    return Encoded(payload, chunk_bits[:nc], cwo, sub_off[:pc_num_substreams(n, chunk)], n, chunk, status)
 
 
 def _decode(fn, name, d_cb, enc: Encoded, payload_words=None, out=None, status=None):

@@ -1,9 +1,13 @@
 // C-ABI entry points of libpc.so that touch the device: argument checks,
 // launch geometry, and HIP error mapping.  The kernels live in encode.hip,
 // decode.hip and histogram.hip; host-only entry points in codebook.cpp.
+#include <atomic>
+
 #include "pc_internal.h"
 
 namespace {
+
+std::atomic<uint32_t> g_wait_polls{pc::kDefaultWaitPolls};
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -28,6 +32,22 @@ pc_status check_decode_args(const pc_codebook *d_cb, const uint32_t *d_payload, 
     return PC_OK;
 }
 
+pc_status check_encode_args(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size_t chunk,
+                            uint32_t *d_payload, size_t payload_capacity_words, uint32_t *d_chunk_bits,
+                            uint64_t *d_chunk_word_offset, uint32_t *d_sub_off, uint32_t *d_status) {
+    if (!chunk_ok(chunk) || !d_chunk_word_offset || !d_status) return PC_ERR_INVALID_ARG;
+    if (!aligned(d_chunk_word_offset, 8) || !aligned(d_status, 4)) return PC_ERR_INVALID_ARG;
+    if (n > 0) {
+        if (!d_cb || !d_in || !d_payload || !d_chunk_bits || !d_sub_off) return PC_ERR_INVALID_ARG;
+        if (!aligned(d_cb, 16) || !aligned(d_in, 16) || !aligned(d_payload, 16) || !aligned(d_chunk_bits, 4) ||
+            !aligned(d_sub_off, 4))
+            return PC_ERR_INVALID_ARG;
+        if (pc_num_chunks(n, chunk) > 0x7FFFFFFFull) return PC_ERR_UNSUPPORTED;
+        if (payload_capacity_words < pc_max_payload_words(n, chunk)) return PC_ERR_CAPACITY;
+    }
+    return PC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -37,22 +57,21 @@ size_t pc_encode_workspace_bytes(size_t n, size_t chunk) {
     return (1 + pc_num_chunks(n, chunk)) * sizeof(uint64_t);
 }
 
+uint32_t pc_encode_set_wait_limit(uint32_t polls) {
+    return g_wait_polls.exchange(polls ? polls : pc::kDefaultWaitPolls);
+}
+
 pc_status pc_encode(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size_t chunk, uint32_t *d_payload,
                     size_t payload_capacity_words, uint32_t *d_chunk_bits, uint64_t *d_chunk_word_offset,
-                    uint32_t *d_sub_off, void *d_ws, size_t ws_bytes, void *stream) {
-    if (!chunk_ok(chunk) || !d_chunk_word_offset || !d_ws) return PC_ERR_INVALID_ARG;
-    if (!aligned(d_chunk_word_offset, 8) || !aligned(d_ws, 8)) return PC_ERR_INVALID_ARG;
-    if (n > 0) {
-        if (!d_cb || !d_in || !d_payload || !d_chunk_bits || !d_sub_off) return PC_ERR_INVALID_ARG;
-        if (!aligned(d_cb, 16) || !aligned(d_in, 16) || !aligned(d_payload, 16) || !aligned(d_chunk_bits, 4) ||
-            !aligned(d_sub_off, 4))
-            return PC_ERR_INVALID_ARG;
-        if (pc_num_chunks(n, chunk) > 0x7FFFFFFFull) return PC_ERR_UNSUPPORTED;
-        if (payload_capacity_words < pc_max_payload_words(n, chunk)) return PC_ERR_CAPACITY;
-    }
+                    uint32_t *d_sub_off, void *d_ws, size_t ws_bytes, uint32_t *d_status, void *stream) {
+    pc_status st = check_encode_args(d_cb, d_in, n, chunk, d_payload, payload_capacity_words, d_chunk_bits,
+                                     d_chunk_word_offset, d_sub_off, d_status);
+    if (st != PC_OK) return st;
+    if (!d_ws || !aligned(d_ws, 8)) return PC_ERR_INVALID_ARG;
     if (ws_bytes < pc_encode_workspace_bytes(n, chunk)) return PC_ERR_CAPACITY;
     return map_hip(pc::launch_encode(d_cb, d_in, n, (uint32_t)chunk, d_payload, d_chunk_bits, d_chunk_word_offset,
-                                     d_sub_off, static_cast<uint64_t *>(d_ws), static_cast<hipStream_t>(stream)));
+                                     d_sub_off, static_cast<uint64_t *>(d_ws), d_status,
+                                     g_wait_polls.load(std::memory_order_relaxed), static_cast<hipStream_t>(stream)));
 }
 
 pc_status pc_decode(const pc_codebook *d_cb, const uint32_t *d_payload, size_t payload_words,

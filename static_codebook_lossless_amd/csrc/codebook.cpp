@@ -30,7 +30,8 @@ namespace {
 constexpr int kN = PC_ALPHABET;
 constexpr int kL = PC_MAX_LEN;
 
-// Package-merge (coin collector) for n = 256 weights and depth limit L.
+// Package-merge (coin collector) for n weights (2 <= n <= 256) and depth
+// limit L.
 //
 // Level lists are built bottom-up: the deepest list is the sorted leaves;
 // each shallower list merges the leaves with the pairs ("packages") of the
@@ -39,30 +40,30 @@ constexpr int kL = PC_MAX_LEN;
 // consecutive pairs and lists are merged in order, the selected items of
 // every level form a prefix of that level's list; a leaf's code length is
 // the number of levels whose selected prefix contains it.
-void package_merge_lengths(const uint64_t *w, uint8_t *len_out) {
+void package_merge_lengths(const uint64_t *w, int n, uint8_t *len_out) {
     int order[kN];
-    for (int i = 0; i < kN; ++i) order[i] = i;
-    std::stable_sort(order, order + kN, [&](int a, int b) {
+    for (int i = 0; i < n; ++i) order[i] = i;
+    std::stable_sort(order, order + n, [&](int a, int b) {
         return w[a] < w[b] || (w[a] == w[b] && a < b);
     });
-    std::vector<uint64_t> leafw(kN);
-    for (int i = 0; i < kN; ++i) leafw[i] = w[order[i]];
+    std::vector<uint64_t> leafw(n);
+    for (int i = 0; i < n; ++i) leafw[i] = w[order[i]];
 
     // is_pkg[level][k]: whether item k of the level's list is a package.
     // Level 0 is the deepest list (leaves only), level L-1 the top.
     std::vector<std::vector<uint8_t>> is_pkg(kL);
     std::vector<uint64_t> cur(leafw);
-    is_pkg[0].assign(kN, 0);
+    is_pkg[0].assign(n, 0);
     for (int lev = 1; lev < kL; ++lev) {
         const size_t npk = cur.size() / 2;
         std::vector<uint64_t> next;
         std::vector<uint8_t> flags;
-        next.reserve(kN + npk);
-        flags.reserve(kN + npk);
+        next.reserve(n + npk);
+        flags.reserve(n + npk);
         size_t i = 0, j = 0;
-        while (i < (size_t)kN || j < npk) {
+        while (i < (size_t)n || j < npk) {
             uint64_t pw = j < npk ? cur[2 * j] + cur[2 * j + 1] : 0;
-            bool take_leaf = j >= npk || (i < (size_t)kN && leafw[i] <= pw);
+            bool take_leaf = j >= npk || (i < (size_t)n && leafw[i] <= pw);
             if (take_leaf) {
                 next.push_back(leafw[i++]);
                 flags.push_back(0);
@@ -79,7 +80,7 @@ void package_merge_lengths(const uint64_t *w, uint8_t *len_out) {
     // leaves in the prefix each gain one bit; the packages in it select a
     // prefix of twice their number in the level below.
     int depth[kN] = {0};
-    size_t m = 2 * kN - 2;
+    size_t m = 2 * (size_t)n - 2;
     for (int lev = kL - 1; lev >= 0; --lev) {
         size_t leaves = 0, pkgs = 0;
         const auto &f = is_pkg[lev];
@@ -87,7 +88,7 @@ void package_merge_lengths(const uint64_t *w, uint8_t *len_out) {
         for (size_t k = 0; k < leaves; ++k) depth[k]++;
         m = 2 * pkgs;
     }
-    for (int i = 0; i < kN; ++i) len_out[order[i]] = (uint8_t)depth[i];
+    for (int i = 0; i < n; ++i) len_out[order[i]] = (uint8_t)depth[i];
 }
 
 // Canonical code values: symbols in (length, byte value) order, consecutive
@@ -175,6 +176,7 @@ const char *pc_status_string(int status) {
         case PC_ERR_CAPACITY: return "buffer too small";
         case PC_ERR_CORRUPT: return "corrupt stream";
         case PC_ERR_HIP: return "HIP runtime error";
+        case PC_ERR_TIMEOUT: return "device wait gave up";
         default: return "unknown status";
     }
 }
@@ -191,7 +193,7 @@ pc_status pc_codebook_build(const uint64_t counts[256], int kind, const uint8_t 
         if (qlc_bits) return PC_ERR_INVALID_ARG;
         uint64_t w[kN];
         for (int s = 0; s < kN; ++s) w[s] = counts[s] ? counts[s] : 1;  // every byte stays codable
-        package_merge_lengths(w, cb.length);
+        package_merge_lengths(w, kN, cb.length);
         canonical_codes(cb.length, cb.code);
     } else if (kind == PC_CODEBOOK_QLC) {
         if (!qlc_bits || !qlc_bits_ok(qlc_bits)) return PC_ERR_INVALID_ARG;
@@ -259,6 +261,28 @@ pc_status pc_codebook_fit(const pc_codebook *cb, const uint64_t counts[256], dou
     }
     *avg_bits = (double)(bits / total);
     *entropy = (double)h;
+    return PC_OK;
+}
+
+// The comparator of a per-shard ("three-stage") code: package-merge on the
+// shard's own counts over the byte values that occur, so an absent value
+// gets no codeword; one present value gets a 1-bit code.
+pc_status pc_shard_code_lengths(const uint64_t counts[256], uint8_t lengths_out[256]) {
+    if (!counts || !lengths_out) return PC_ERR_INVALID_ARG;
+    uint64_t w[kN];
+    int sym[kN], n = 0;
+    for (int s = 0; s < kN; ++s) {
+        lengths_out[s] = 0;
+        if (counts[s]) {
+            w[n] = counts[s];
+            sym[n++] = s;
+        }
+    }
+    if (n == 1) lengths_out[sym[0]] = 1;
+    if (n < 2) return PC_OK;
+    uint8_t sub[kN];
+    package_merge_lengths(w, n, sub);
+    for (int i = 0; i < n; ++i) lengths_out[sym[i]] = sub[i];
     return PC_OK;
 }
 

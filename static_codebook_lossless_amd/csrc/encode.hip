@@ -47,11 +47,13 @@ __device__ __forceinline__ void st_desc(uint64_t *p, uint64_t v) {
 // sums counts up to the nearest inclusive prefix, or walks 128 chunks
 // further back.  (Descriptors written on other dies are read through the
 // fabric: more loads per poll made each trip slower, measured.)
-// The wait on predecessors is bounded: it always ends once they publish,
-// but should an ordering bug ever leave a predecessor silent, the wave gives
-// up after ~2^20 polls (about a second) and sets bit 32 of workspace word 0
-// instead of spinning forever.
-constexpr uint32_t kMaxPolls = 1u << 20;
+// The wait on predecessors is bounded: it ends once they publish, but a
+// predecessor that stays silent longer than max_polls polls (by default
+// ~2^20, about a second: a workgroup preempted for that long, or a bug) makes
+// the wave give up instead of spinning forever.  It then reports
+// PC_ERR_TIMEOUT through *status and publishes an inclusive prefix that
+// assumes nothing before it (the caller discards the output), so that its
+// successors' walks end there instead of each waiting out its own limit.
 constexpr int kLookWin = 2;  // descriptors per lane per round
 
 // Publish descriptor c's own count: inclusive for c == 0, else aggregate.
@@ -60,7 +62,8 @@ __device__ __forceinline__ void publish_count(uint64_t *desc, uint32_t c, uint64
 }
 
 // `published`: the caller already ran publish_count for c.
-__device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_t lane, bool published = false) {
+__device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_t lane, uint32_t max_polls,
+                             uint32_t *status, bool published = false) {
     if (c == 0) {
         if (lane == 0 && !published) st_desc(&desc[0], kDescInclusive | words);
         return 0;
@@ -88,8 +91,11 @@ __device__ uint64_t lookback(uint64_t *desc, uint32_t c, uint64_t words, uint32_
                 any |= wait[w];
             }
             if (!__any(any)) break;
-            if (polls == kMaxPolls) {
-                if (lane == 0) atomicOr(reinterpret_cast<unsigned long long *>(desc - 1), 1ull << 32);
+            if (polls + 1 >= max_polls) {
+                if (lane == 0) {
+                    atomicCAS(status, 0u, (uint32_t)PC_ERR_TIMEOUT);
+                    st_desc(&desc[c], kDescInclusive | words);
+                }
                 return 0;
             }
         }
@@ -291,7 +297,8 @@ template <uint32_t THREADS, int NT, uint32_t BUFW, int TPC>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS == 1024 ? 8 : 1))) void encode_chunk_kernel(
     const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint64_t n, uint32_t chunk,
     uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
-    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws) {
+    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws,
+    uint32_t *__restrict__ status, uint32_t max_polls) {
     using SH = ChunkShared<THREADS, NT, BUFW>;
     constexpr uint32_t TILE = THREADS * kSymPerLane;
     constexpr uint32_t NW = THREADS / 64;
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
         }
         __syncthreads();
         if (wave == 0) {
-            const uint64_t excl = lookback(ws + 1, s, words, lane, kHold > 0);
+            const uint64_t excl = lookback(ws + 1, s, words, lane, max_polls, status, kHold > 0);
             if (lane == 0) {
                 sh.misc[1] = (uint32_t)excl;
                 sh.misc[2] = (uint32_t)(excl >> 32);
@@ -450,7 +457,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
     const uint64_t words = tb[NT] >> 5;
     for (uint32_t i = tid; i < (BUFW + 8) / 4; i += THREADS) reinterpret_cast<uint4 *>(sh.buf)[i] = make_uint4(0, 0, 0, 0);
     if (wave == 0) {
-        const uint64_t excl = lookback(ws + 1, s, words, lane);
+        const uint64_t excl = lookback(ws + 1, s, words, lane, max_polls, status);
         if (lane == 0) {
             sh.misc[1] = (uint32_t)excl;
             sh.misc[2] = (uint32_t)(excl >> 32);
@@ -498,7 +505,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
 __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint64_t n, uint32_t chunk,
     uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
-    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws, uint32_t coff) {
+    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws, uint32_t coff,
+    uint32_t *__restrict__ status, uint32_t max_polls) {
     using SH = Shared<kThreads>;
     __shared__ SH sh;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -527,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     const uint32_t total = uniform(sh.wave_tot[0][0] + sh.wave_tot[0][1] + sh.wave_tot[0][2] + sh.wave_tot[0][3]);
     const uint64_t words = (total + 31) >> 5;
     if (wave == 0) {
-        const uint64_t excl = lookback(ws + 1, t, words, lane);
+        const uint64_t excl = lookback(ws + 1, t, words, lane, max_polls, status);
         if (lane == 0) {
             sh.misc[1] = (uint32_t)excl;
             sh.misc[2] = (uint32_t)(excl >> 32);
@@ -566,25 +574,28 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     }
 }
 
-// Zero the ticket and the look-back descriptors; write the total-word entry
-// for an empty input.
-__global__ void encode_init_kernel(uint64_t *ws, uint64_t ws_words, uint64_t *cwo, int empty) {
+// Zero the ticket, the look-back descriptors and the status word; write the
+// total-word entry for an empty input.
+__global__ void encode_init_kernel(uint64_t *ws, uint64_t ws_words, uint64_t *cwo, int empty, uint32_t *status) {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t k = i; k < ws_words; k += stride) ws[k] = 0;
-    if (empty && i == 0) cwo[0] = 0;
+    if (i == 0) {
+        *status = 0;
+        if (empty) cwo[0] = 0;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, uint32_t chunk,
                          uint32_t *payload, uint32_t *chunk_bits, uint64_t *cwo, uint32_t *sub_off,
-                         uint64_t *ws, hipStream_t stream) {
+                         uint64_t *ws, uint32_t *status, uint32_t max_polls, hipStream_t stream) {
     const uint64_t nc = (n + chunk - 1) / chunk;
     const uint64_t ws_words = 1 + nc;
     const uint32_t init_blocks = (uint32_t)((ws_words + 255) / 256 < 1024 ? (ws_words + 255) / 256 : 1024);
     hipLaunchKernelGGL(encode_init_kernel, dim3(init_blocks ? init_blocks : 1), dim3(256), 0, stream, ws,
-                       ws_words, cwo, n == 0 ? 1 : 0);
+                       ws_words, cwo, n == 0 ? 1 : 0, status);
     if (n == 0) return hipGetLastError();
     const uint64_t nfull = n / chunk;  // chunks of exactly `chunk` symbols
     // Full chunks go to workgroups of NT tiles (TPC tiles per chunk, so
@@ -606,7 +617,7 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
         if (nsup) {                                                                                        \
             hipLaunchKernelGGL((encode_chunk_kernel<T, NT, BW, TPC>), dim3((uint32_t)nsup), dim3(T), 0,    \
                                stream, cb, in, n, chunk, (uint32_t)nc, payload, chunk_bits, cwo, sub_off,  \
-                               ws);                                                                        \
+                               ws, status, max_polls);                                                     \
             done = nsup * ((NT) / (TPC));                                                                  \
             tickets = nsup;                                                                                \
         }                                                                                               \
@@ -623,7 +634,8 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
     // chunk t + done - tickets
     if (rest)
         hipLaunchKernelGGL(encode_kernel_any, dim3((uint32_t)rest), dim3(kThreads), 0, stream, cb, in, n, chunk,
-                           (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws, (uint32_t)(done - tickets));
+                           (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws, (uint32_t)(done - tickets), status,
+                           max_polls);
 #undef PC_ENC
     return hipGetLastError();
 }

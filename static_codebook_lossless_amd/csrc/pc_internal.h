@@ -92,9 +92,13 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
 // Launchers (defined in the .hip files, called from api.hip).
 // ---------------------------------------------------------------------------
 
+// max_polls: polls of the cross-chunk scan's bounded wait before it gives up
+// and writes PC_ERR_TIMEOUT to *status (which the launch first zeroes).
+constexpr uint32_t kDefaultWaitPolls = 1u << 20;
+
 hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, uint32_t chunk,
                          uint32_t *payload, uint32_t *chunk_bits, uint64_t *cwo, uint32_t *sub_off,
-                         uint64_t *ws, hipStream_t stream);
+                         uint64_t *ws, uint32_t *status, uint32_t max_polls, hipStream_t stream);
 
 enum DecodeMode { kDecodeLut12 = 0, kDecodeQlc = 1 };
 

@@ -14,10 +14,11 @@ ODD = P((1 << 20) + 4)  # 4-byte aligned only
 CHUNK = 65536
 
 
-def enc(cb=A, x=A, n=1000, chunk=CHUNK, payload=A, cap=None, bits=A, cwo=A, sub=A, ws=A, ws_bytes=None):
+def enc(cb=A, x=A, n=1000, chunk=CHUNK, payload=A, cap=None, bits=A, cwo=A, sub=A, ws=A, ws_bytes=None,
+        status=A):
     cap = pc.pc_max_payload_words(n, chunk) if cap is None else cap
     ws_bytes = pc.pc_encode_workspace_bytes(n, chunk) if ws_bytes is None else ws_bytes
-    return lib.pc_encode(cb, x, n, chunk, payload, cap, bits, cwo, sub, ws, ws_bytes, None)
+    return lib.pc_encode(cb, x, n, chunk, payload, cap, bits, cwo, sub, ws, ws_bytes, status, None)
 
 
 def dec(fn, cb=A, payload=A, words=100, bits=A, cwo=A, sub=A, n=1000, chunk=CHUNK, out=A, status=A):
@@ -33,7 +34,7 @@ def test_bad_chunk_sizes(chunk):
     assert pc.pc_encode_workspace_bytes(1000, chunk) == 0
 
 
-@pytest.mark.parametrize("which", ["cb", "x", "payload", "bits", "cwo", "sub", "ws"])
+@pytest.mark.parametrize("which", ["cb", "x", "payload", "bits", "cwo", "sub", "ws", "status"])
 def test_encode_null_pointers(which):
     assert enc(**{which: None}) == pc.PC_ERR_INVALID_ARG
 
@@ -41,6 +42,16 @@ def test_encode_null_pointers(which):
 @pytest.mark.parametrize("which", ["cb", "x", "payload", "cwo", "ws"])
 def test_encode_misaligned_pointers(which):
     assert enc(**{which: ODD}) == pc.PC_ERR_INVALID_ARG
+    assert enc(status=P((1 << 20) + 2)) == pc.PC_ERR_INVALID_ARG
+
+
+def test_encode_wait_limit_round_trips():
+    prev = pc.pc_encode_set_wait_limit(7)
+    try:
+        assert pc.pc_encode_set_wait_limit(0) == 7
+        assert pc.pc_encode_set_wait_limit(0) == prev  # 0 restores the default
+    finally:
+        pc.pc_encode_set_wait_limit(prev)
 
 
 def test_encode_capacity():

@@ -98,6 +98,35 @@ def test_size_queries_match_oracle(n, chunk):
     assert pc.pc_encode_workspace_bytes(n, chunk) >= 8 * (1 + coder.num_chunks(n, chunk))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_shard_code_lengths_match_oracle(seed):
+    rng = np.random.default_rng(90 + seed)
+    counts = rng.integers(0, 10**6, 256)
+    counts[rng.random(256) < [0.0, 0.1, 0.5, 0.9, 0.98, 0.3][seed]] = 0  # absent byte values
+    if seed == 5:
+        counts = (rng.pareto(0.7, 256) * 10).astype(np.int64)  # skewed: the 12-bit limit binds
+    got = pc.pc_shard_code_lengths(counts)
+    want = cb.per_shard_lengths([int(c) for c in counts])
+    assert got.tolist() == want
+
+
+@pytest.mark.parametrize("name", ["normal_1m", "int8_weight"])
+def test_shard_code_lengths_match_oracle_on_workloads(name):
+    counts = np.bincount(W.make(name, 0), minlength=256)
+    assert pc.pc_shard_code_lengths(counts).tolist() == cb.per_shard_lengths([int(c) for c in counts])
+
+
+def test_shard_code_lengths_degenerate():
+    assert pc.pc_shard_code_lengths(np.zeros(256, dtype=np.uint64)).tolist() == [0] * 256
+    one = np.zeros(256, dtype=np.uint64)
+    one[9] = 5
+    got = pc.pc_shard_code_lengths(one)
+    assert got[9] == 1 and int(got.sum()) == 1
+    two = np.zeros(256, dtype=np.uint64)
+    two[[0, 255]] = [3, 1000]
+    assert pc.pc_shard_code_lengths(two)[[0, 255]].tolist() == [1, 1]
+
+
 @pytest.mark.parametrize("seed", range(2))
 def test_qlc_optimal_bits_matches_exhaustive_search(seed):
     rng = np.random.default_rng(70 + seed)

@@ -44,6 +44,7 @@ def gpu_encode(dcb, x_np, chunk):
     x = torch.from_numpy(x_np).to(DEV)
     enc = pc.pc_encode(dcb, x, chunk)
     torch.cuda.synchronize()
+    assert int(enc.status.item()) == pc.PC_OK
     return x, enc
 
 
@@ -165,6 +166,7 @@ def test_edge_sizes(chunk):
                 enc = pc.pc_encode(dcb, x, chunk)
                 torch.cuda.synchronize()
                 assert int(enc.chunk_word_offset[0].item()) == 0
+                assert int(enc.status.item()) == pc.PC_OK
                 out, status = pc.pc_decode(dcb, enc)
                 torch.cuda.synchronize()
                 assert out.numel() == 0 and int(status.item()) == 0
@@ -441,6 +443,7 @@ def test_side_streams_and_reused_buffers():
         for i in range(2):
             want = coder.encode(inputs[i], obook["lengths"], obook["codes"], chunk, threads=4)
             assert_same_stream(host(encs[i]), want)
+            assert int(encs[i].status.item()) == pc.PC_OK
             assert int(stats[i].item()) == 0
             assert torch.equal(dec_out[i][:inputs[i].size], xs[i])
         for i in range(2):  # stale contents for the second pass
@@ -458,3 +461,37 @@ def test_largest_chunk_size():
     for n in (chunk + 12345, 3 * (1 << 20) + 7):
         say("largest chunk:", chunk, "n", n)
         roundtrip(dcb, obook, skewed(n, n % 1000), chunk)
+
+
+def test_encode_wait_give_up_is_reported():
+    """The cross-chunk scan's bounded wait, cut to one poll from the host, gives
+    up while earlier workgroups are still running and reports PC_ERR_TIMEOUT
+    through the status word (every kernel still ends normally: no wait is
+    longer than one poll).  With the default limit the same call is correct
+    again.  1024 workgroups of 4 chunks: the first 512 run at once, so many
+    look-backs meet an unpublished predecessor on their first poll."""
+    w = W.WORKLOADS["ffn1_act"]
+    x_np = W.make("ffn1_act", 0)
+    dcb, obook = make_book(np.bincount(W.make("ffn1_act", 1), minlength=256))
+    x = torch.from_numpy(x_np).to(DEV)
+    outs = pc.alloc_encode_outputs(x_np.size, w.chunk, torch.device(DEV))
+    seen = []
+    prev = pc.pc_encode_set_wait_limit(1)
+    try:
+        for rep in range(3):
+            say("wait give-up: call", rep)
+            enc = pc.pc_encode(dcb, x, w.chunk, outputs=outs)
+            torch.cuda.synchronize()
+            seen.append(int(enc.status.item()))
+            if seen[-1] == pc.PC_ERR_TIMEOUT:
+                break
+    finally:
+        pc.pc_encode_set_wait_limit(prev)
+    say("wait give-up: statuses", seen)
+    assert set(seen) <= {pc.PC_OK, pc.PC_ERR_TIMEOUT}
+    assert pc.PC_ERR_TIMEOUT in seen
+    enc = pc.pc_encode(dcb, x, w.chunk, outputs=outs)
+    torch.cuda.synchronize()
+    assert int(enc.status.item()) == pc.PC_OK
+    want = coder.encode(x_np, obook["lengths"], obook["codes"], w.chunk, threads=8)
+    assert_same_stream(host(enc), want)

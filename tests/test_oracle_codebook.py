@@ -315,6 +315,97 @@ def test_gibbs_fixed_code_costs_at_least_entropy(seed):
     assert cb.coded_bits(cur, shard) <= cb.coded_bits(cur, lengths)
 
 
+# --------------------------------------------------------------------------
+# per-shard comparator ("Single-Stage Huffman Encoder for ML Compression",
+# abstract: the fixed code is compared with Huffman codes built per shard)
+# --------------------------------------------------------------------------
+
+def test_per_shard_code_gives_absent_bytes_no_codeword():
+    # four byte values that occur equally often: a code over just those four
+    # is four 2-bit codewords, and the 252 absent values get none.  A build
+    # that floors absent values to weight 1 codes all 256 values and gives
+    # the four present ones lengths of 5-6 bits instead.
+    counts = [0] * 256
+    for s in (3, 77, 128, 255):
+        counts[s] = 10
+    lengths = cb.per_shard_lengths(counts)
+    assert [lengths[s] for s in (3, 77, 128, 255)] == [2, 2, 2, 2]
+    assert sum(lengths) == 8
+    assert cb.coded_bits(counts, lengths) == 80
+
+
+def test_per_shard_pins_reject_a_floored_build():
+    # the mistake the pins above guard against: flooring absent values to
+    # weight 1 (as the fixed codebook must) before building the shard's code
+    counts = [0] * 256
+    for s in (3, 77, 128, 255):
+        counts[s] = 10
+    floored = cb.package_merge(cb.floor_weights(counts))
+    assert [floored[s] for s in (3, 77, 128, 255)] != [2, 2, 2, 2]
+    assert cb.coded_bits(counts, floored) > 80
+
+
+def test_per_shard_code_dyadic_present_bytes():
+    # counts 8, 4, 2, 1, 1 (probabilities 1/2 .. 1/16) on five scattered byte
+    # values: the optimal code has lengths -log2 p = 1, 2, 3, 4, 4 and costs
+    # exactly the entropy, 16 * 1.875 = 30 bits
+    counts = [0] * 256
+    for s, c in ((200, 8), (5, 4), (17, 2), (0, 1), (99, 1)):
+        counts[s] = c
+    lengths = cb.per_shard_lengths(counts)
+    assert [lengths[s] for s in (200, 5, 17, 0, 99)] == [1, 2, 3, 4, 4]
+    assert sum(1 for v in lengths if v) == 5
+    assert cb.coded_bits(counts, lengths) == 30
+    assert cb.coded_bits(counts, lengths) == pytest.approx(16 * cb.entropy_bits(counts))
+
+
+def test_per_shard_code_degenerate_histograms():
+    one = [0] * 256
+    one[42] = 1000
+    lengths = cb.per_shard_lengths(one)
+    assert lengths[42] == 1 and sum(lengths) == 1  # a lone byte value still takes one bit
+    assert cb.per_shard_lengths([0] * 256) == [0] * 256
+
+
+# --------------------------------------------------------------------------
+# exhaustive QLC layout search (the best 8 area widths for a ranked PMF;
+# "Quad Length Codes for Lossless Compression of e4m3", abstract: the scheme
+# adapts to the distribution)
+# --------------------------------------------------------------------------
+
+def test_qlc_search_uniform_counts():
+    # 256 equally likely bytes: every prefix code spends >= 8 bits a symbol,
+    # with equality only when every length is 8, and a QLC length 3 + b is 8
+    # only for b = 5, which 8 areas of 32 ranks give: the unique optimum
+    assert cb.qlc_optimal_bits_bruteforce([7] * 256) == (5,) * 8
+
+
+def test_qlc_search_dyadic_counts():
+    # Widths (1,1,2,3,4,5,6,7) cover exactly 256 ranks and every area adds
+    # 2^b * 2^-(3+b) = 1/8 to the Kraft sum: a complete code.  Give rank r the
+    # count 2^(10 - length(r)) (64,64,64,64, 32 x4, 16 x8, ..., 1 x128: 1024
+    # in all).  Then every length is -log2 p and the cost is the entropy, the
+    # least any prefix code can spend; by Gibbs' inequality a layout of equal
+    # cost has the same length at every rank, which fixes all 8 widths.
+    widths = (1, 1, 2, 3, 4, 5, 6, 7)
+    per_rank = [1 << (10 - (3 + b)) for b in widths for _ in range(1 << b)]
+    assert len(per_rank) == 256 and sum(per_rank) == 1024
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(256)  # scatter the ranks over the byte values
+    counts = [0] * 256
+    for r, s in enumerate(perm):
+        counts[int(s)] = per_rank[r]
+    assert cb.qlc_optimal_bits_bruteforce(counts) == widths
+    assert cb.qlc_cost(counts, widths) == 6784  # = 1024 * entropy (6.625 bits)
+    assert cb.qlc_cost(counts, widths) == pytest.approx(1024 * cb.entropy_bits(counts))
+
+
+def test_qlc_search_ties_take_the_smallest_vector():
+    # with no counts every covering layout costs 0; the lexicographically
+    # smallest covering vector is seven 1-slot areas and a 256-slot last one
+    assert cb.qlc_optimal_bits_bruteforce([0] * 256) == (0, 0, 0, 0, 0, 0, 0, 8)
+
+
 def test_compressibility_reading():
     assert cb.compressibility(8.0) == 0.0
     assert cb.compressibility(6.728) == pytest.approx(0.159)
