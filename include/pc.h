@@ -213,6 +213,23 @@ pc_status pc_encode(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size
                     void *d_ws, size_t ws_bytes, uint32_t *d_status, void *stream);
 
 /*
+ * pc_encode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, outputs, status word and errors as pc_encode, without the
+ * workspace: the cross-chunk scan's ticket and descriptors live in a static
+ * device array of the library (8 MiB + 8 bytes per GPU, held until the
+ * process ends), so the call allocates nothing.  At most 2^20 chunks per
+ * call (PC_ERR_CAPACITY beyond).  Every call on one GPU shares that GPU's
+ * array and clears it first on its stream: calls that overlap on one GPU
+ * (several streams, or host threads) race and must be serialised by the
+ * caller, e.g. by issuing them on one stream.
+ */
+pc_status pc_encode_noalloc(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size_t chunk,
+                            uint32_t *d_payload, size_t payload_capacity_words,
+                            uint32_t *d_chunk_bits, uint64_t *d_chunk_word_offset, uint32_t *d_sub_off,
+                            uint32_t *d_status, void *stream);
+
+/*
  * Bound of the encoder's one device-side wait (host, process-wide; returns
  * the previous bound).  The pages describe no GPU encoder; this library's
  * chunks learn their output offsets from a single-pass scan in which a

@@ -26,7 +26,7 @@ EXPORTS = [
     "pc_status_string", "pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits", "pc_codebook_fit",
     "pc_shard_code_lengths",
     "pc_num_chunks", "pc_num_substreams", "pc_max_payload_words", "pc_encode_workspace_bytes",
-    "pc_encode", "pc_encode_set_wait_limit", "pc_decode", "pc_decode_qlc", "pc_histogram",
+    "pc_encode", "pc_encode_noalloc", "pc_encode_set_wait_limit", "pc_decode", "pc_decode_qlc", "pc_histogram",
 ]
 
 
@@ -53,13 +53,14 @@ def _load():
         getattr(lib, f).argtypes = [sz, sz]
         getattr(lib, f).restype = sz
     lib.pc_encode.argtypes = [p, p, sz, sz, p, sz, p, p, p, p, sz, p, p]
+    lib.pc_encode_noalloc.argtypes = [p, p, sz, sz, p, sz, p, p, p, p, p]
     lib.pc_encode_set_wait_limit.argtypes = [C.c_uint32]
     lib.pc_encode_set_wait_limit.restype = C.c_uint32
     lib.pc_decode.argtypes = [p, p, sz, p, p, p, sz, sz, p, p, p]
     lib.pc_decode_qlc.argtypes = [p, p, sz, p, p, p, sz, sz, p, p, p]
     lib.pc_histogram.argtypes = [p, sz, p, p]
     for f in ("pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits", "pc_codebook_fit",
-              "pc_shard_code_lengths", "pc_encode",
+              "pc_shard_code_lengths", "pc_encode", "pc_encode_noalloc",
               "pc_decode", "pc_decode_qlc", "pc_histogram"):
         getattr(lib, f).restype = i
     return lib
@@ -222,6 +223,23 @@ def pc_encode(d_cb: torch.Tensor, d_in: torch.Tensor, chunk: int, outputs=None) 
     st = lib.pc_encode(_ptr(d_cb), _ptr(x), n, chunk, _ptr(payload), payload.numel(), _ptr(chunk_bits),
                        _ptr(cwo), _ptr(sub_off), _ptr(ws), ws.numel() * 8, _ptr(status), _stream(x.device))
     _check(st, "pc_encode")
+    nc = pc_num_chunks(n, chunk)
+    return Encoded(payload, chunk_bits[:nc], cwo, sub_off[:pc_num_substreams(n, chunk)], n, chunk, status)
+
+
+def pc_encode_noalloc(d_cb: torch.Tensor, d_in: torch.Tensor, chunk: int, outputs=None) -> Encoded:
+    """``pc_encode`` through the entry point that allocates nothing on the
+    device: its workspace is the library's own static array (at most 2^20
+    chunks; calls that overlap on one GPU race).  The workspace entry of
+    ``outputs`` is not used."""
+    if d_in.dtype != torch.uint8 or not d_in.is_cuda:
+        raise TypeError("d_in must be a uint8 CUDA tensor")
+    x = d_in.reshape(-1)
+    n = x.numel()
+    payload, chunk_bits, cwo, sub_off, _, status = outputs or alloc_encode_outputs(n, chunk, x.device)
+    st = lib.pc_encode_noalloc(_ptr(d_cb), _ptr(x), n, chunk, _ptr(payload), payload.numel(), _ptr(chunk_bits),
+                               _ptr(cwo), _ptr(sub_off), _ptr(status), _stream(x.device))
+    _check(st, "pc_encode_noalloc")
     nc = pc_num_chunks(n, chunk)
     return Encoded(payload, chunk_bits[:nc], cwo, sub_off[:pc_num_substreams(n, chunk)], n, chunk, status)
 

@@ -5,9 +5,42 @@
 
 #include "pc_internal.h"
 
+// Workspace of pc_encode_noalloc: the ticket word and one look-back
+// descriptor per workgroup unit (at most one per chunk), for up to
+// kNoAllocMaxChunks chunks: 8 MiB + 8 bytes on every GPU the library runs
+// on, held until the process ends.  Host code never uses the array's name
+// as an address: each device's copy is reached through the pointer
+// hipGetSymbolAddress returns for it (noalloc_scratch below).
+static constexpr size_t kNoAllocMaxChunks = (size_t)1 << 20;
+static __device__ __align__(256) uint64_t scratch[1 + kNoAllocMaxChunks];
+
 namespace {
 
 std::atomic<uint32_t> g_wait_polls{pc::kDefaultWaitPolls};
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint64_t *> g_scratch_of[kMaxDevices];
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current).  Concurrent first calls may both look it up; they
+// store the same address.
+hipError_t noalloc_scratch(uint64_t **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    uint64_t *p = g_scratch_of[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!addr) return hipErrorInvalidSymbol;
+        p = static_cast<uint64_t *>(addr);
+        g_scratch_of[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -72,6 +105,21 @@ pc_status pc_encode(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size
     return map_hip(pc::launch_encode(d_cb, d_in, n, (uint32_t)chunk, d_payload, d_chunk_bits, d_chunk_word_offset,
                                      d_sub_off, static_cast<uint64_t *>(d_ws), d_status,
                                      g_wait_polls.load(std::memory_order_relaxed), static_cast<hipStream_t>(stream)));
+}
+
+pc_status pc_encode_noalloc(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size_t chunk,
+                            uint32_t *d_payload, size_t payload_capacity_words, uint32_t *d_chunk_bits,
+                            uint64_t *d_chunk_word_offset, uint32_t *d_sub_off, uint32_t *d_status, void *stream) {
+    pc_status st = check_encode_args(d_cb, d_in, n, chunk, d_payload, payload_capacity_words, d_chunk_bits,
+                                     d_chunk_word_offset, d_sub_off, d_status);
+    if (st != PC_OK) return st;
+    if (pc_num_chunks(n, chunk) > kNoAllocMaxChunks) return PC_ERR_CAPACITY;
+    uint64_t *ws = nullptr;
+    const hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return PC_ERR_HIP;
+    return map_hip(pc::launch_encode(d_cb, d_in, n, (uint32_t)chunk, d_payload, d_chunk_bits, d_chunk_word_offset,
+                                     d_sub_off, ws, d_status, g_wait_polls.load(std::memory_order_relaxed),
+                                     static_cast<hipStream_t>(stream)));
 }
 
 pc_status pc_decode(const pc_codebook *d_cb, const uint32_t *d_payload, size_t payload_words,
