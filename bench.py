@@ -280,6 +280,107 @@ def qlc_leg(pc, W, dev):
                                 "huffman12_compressibility": round(1 - bh / 8, 5)}}
 
 
+def stream_stats(pc, x, enc, n, chunk):
+    """Bits/symbol of an encoded stream: payload, with the side index and
+    chunk tables, order-0 entropy, and the per-shard Huffman-12 comparator
+    (absent byte values excluded)."""
+    import numpy as np
+
+    nc = pc.pc_num_chunks(n, chunk)
+    nsub = pc.pc_num_substreams(n, chunk)
+    cbits = enc.chunk_bits.cpu().numpy().view(np.uint32).astype(np.int64)
+    words = int(enc.chunk_word_offset[nc].item())
+    xc = pc.pc_histogram(x).cpu().numpy().astype(np.float64)
+    p = xc[xc > 0] / n
+    H = float(-(p * np.log2(p)).sum())
+    shard_len = pc.pc_shard_code_lengths(xc.astype(np.uint64)).astype(np.float64)
+    shard = float((xc * shard_len).sum()) / n
+    b = float(cbits.sum()) / n
+    return {"payload": round(b, 5), "with_side_index": round((words * 32 + 32 * nsub + 96 * nc) / n, 5),
+            "entropy": round(H, 5), "per_shard_huffman12": round(shard, 5),
+            "gap_vs_entropy_rel": round(b / H - 1, 5), "gap_vs_per_shard_rel": round(b / shard - 1, 5),
+            "compressibility": round(1 - b / 8, 5)}, words
+
+
+def config_leg(pc, W, name, dev, reps, decoders):
+    """One benchmark configuration: encode and decode times (HIP events on the
+    launch stream, per call), GB/s of uncompressed bytes, HBM roofline
+    fraction on algorithmic bytes, bits/symbol.  Returns the report and the
+    device outputs (for the oracle comparison of the cpu_baseline leg)."""
+    import numpy as np
+    import torch
+
+    w = W.WORKLOADS[name]
+    counts = torch.zeros(256, dtype=torch.int64, device=dev)
+    for s in w.prev_seeds:
+        pc.pc_histogram(torch.from_numpy(W.make(name, s)).to(dev), counts)
+    counts_np = counts.cpu().numpy().astype(np.uint64)
+    x_np = W.make(name, 0)
+    x = torch.from_numpy(x_np).to(dev)
+    n, chunk = w.n, w.chunk
+    dcb = pc.pc_codebook_build(counts_np, w.kind, w.qlc_bits).to(dev)
+    outs = pc.alloc_encode_outputs(n, chunk, dev)
+    out = torch.empty(n, dtype=torch.uint8, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    enc_ms = timed(lambda: pc.pc_encode(dcb, x, chunk, outs))
+    enc = pc.pc_encode(dcb, x, chunk, outs)
+    torch.cuda.synchronize()
+    enc_ok = int(enc.status.item()) == 0
+    bits, words = stream_stats(pc, x, enc, n, chunk)
+    alg = n + words * 4 + 4 * pc.pc_num_substreams(n, chunk) + 12 * pc.pc_num_chunks(n, chunk) + 8
+    rep = {"n_bytes": n, "chunk": chunk, "codebook": w.kind, "qlc_bits": list(w.qlc_bits) if w.qlc_bits else None,
+           "algorithmic_bytes": alg, "encode": None, "decode": {}, "bits_per_symbol": bits}
+
+    def line(ms):
+        med = float(np.median(ms))
+        return {"ms": ms_stats(ms), "GBps": round(n / (med * 1e-3) / 1e9, 1),
+                "roofline_frac": round(alg / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    rep["encode"] = line(enc_ms)
+    rep["encode"]["status_ok"] = enc_ok
+    for dname in decoders:
+        fn = pc.pc_decode_qlc if dname == "qlc" else pc.pc_decode
+        st.zero_()
+        dec_ms = timed(lambda: fn(dcb, enc, out=out, status=st))
+        torch.cuda.synchronize()
+        rep["decode"][dname] = line(dec_ms)
+        rep["decode"][dname]["round_trip_ok"] = bool(int(st.item()) == 0 and torch.equal(out, x))
+    host = {"payload": enc.payload[:words].cpu().numpy().view(np.uint32).copy(),
+            "chunk_bits": enc.chunk_bits.cpu().numpy().view(np.uint32).copy(),
+            "chunk_word_offset": enc.chunk_word_offset.cpu().numpy().view(np.uint64).copy(),
+            "sub_off": enc.sub_off.cpu().numpy().view(np.uint32).copy()}
+    return rep, (x_np, counts_np, w.kind, w.qlc_bits, chunk, host)
+
+
+def oracle_parity(case, threads):
+    """Part of the cpu_baseline leg: the oracle's bit-serial coder on a whole
+    configuration, every array compared with the GPU's."""
+    import numpy as np
+
+    from oracle import codebook as ocb
+    from oracle import coder
+
+    x_np, counts, kind, qlc_bits, chunk, host = case
+    book = ocb.codebook([int(c) for c in counts], kind, qlc_bits)
+    s = coder.encode(x_np, book["lengths"], book["codes"], chunk, threads=threads)
+    y, rc = coder.decode(s, x_np.size, chunk, book, threads=threads)
+    return {k: bool(np.array_equal(host[k], s[k])) for k in ("payload", "chunk_bits", "chunk_word_offset", "sub_off")} | \
+        {"oracle_round_trip": bool(rc == 0 and np.array_equal(y, x_np))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +394,9 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the QLC (GELU tensor) and histogram measurements")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration lines (configurations 1-4)")
+    ap.add_argument("--config-reps", type=int, default=20)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -438,6 +542,32 @@ def main():
         cpu, parity = cpu_baseline_leg(x_np, counts_prev, w.kind, w.qlc_bits, chunk, host_streams,
                                        args.cpu_seconds, threads)
 
+    per_config = None
+    if not args.no_configs:
+        per_config = {}
+        cases = {}
+        for name in W.CONFIG_ORDER:
+            if name == w.name:
+                continue
+            log("config %s" % name)
+            decs = ["lut12", "qlc"] if W.WORKLOADS[name].kind == "qlc" else ["lut12"]
+            per_config[name], cases[name] = config_leg(pc, W, name, dev, args.config_reps, decs)
+        if not args.no_cpu_baseline:
+            threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(os.cpu_count() or 1, 16)
+            for name, case in cases.items():
+                log("oracle parity %s" % name)
+                per_config[name]["oracle_parity"] = oracle_parity(case, threads)
+        del cases
+        per_config[w.name] = {"n_bytes": n, "chunk": chunk, "headline": True,
+                              "encode": {"ms": ms_stats(enc_ms), "GBps": round(n / (avg["encode"] * 1e-3) / 1e9, 1),
+                                         "roofline_frac": round(alg["encode"] / (avg["encode"] * 1e-3) / 1e9 /
+                                                                HBM_PEAK_GBPS, 4)},
+                              "decode": {args.decoder: {"ms": ms_stats(dec_ms),
+                                                        "GBps": round(n / (avg["decode"] * 1e-3) / 1e9, 1),
+                                                        "roofline_frac": round(alg["decode"] / (avg["decode"] * 1e-3)
+                                                                               / 1e9 / HBM_PEAK_GBPS, 4)}},
+                              "oracle_parity": parity}
+
     secondary = None
     if not args.no_secondary:
         hist_ms = time_calls(lambda: pc.pc_histogram(x), 10)
@@ -479,10 +609,17 @@ def main():
         "round_trip_ok": bool(st == 0 and est == 0 and same),
         "cpu_baseline": cpu,
         "oracle_parity_sample": parity,
+        "per_config": per_config,
         "secondary": secondary,
     }
     print(json.dumps(res), flush=True)
-    return 0 if (st == 0 and est == 0 and same and (parity is None or all(v for k, v in parity.items() if k != "chunks"))) else 1
+    ok = st == 0 and est == 0 and same and (parity is None or all(v for k, v in parity.items() if k != "chunks"))
+    for name, c in (per_config or {}).items():
+        if c.get("headline"):
+            continue
+        ok = ok and c["encode"]["status_ok"] and all(d["round_trip_ok"] for d in c["decode"].values())
+        ok = ok and all(c.get("oracle_parity", {}).values())
+    return 0 if ok else 1
 
 
 if __name__ == "__main__":

@@ -10,28 +10,26 @@
 // persistent and walk the groups with a stride of the grid size.  While a
 // workgroup decodes group k out of LDS, the loads of group k+1 (its
 // container entries, then its payload span into registers, two 16-byte
-// loads per lane after each of the steps 0-8 of the first 128 symbols; the
+// loads per lane after each of the steps 0-7 of the first 128 symbols; the
 // span's entries come one group earlier still) are in flight, so HBM
 // latency is hidden behind decoding.  Per group:
-//   1. the staged span sits in LDS in rows of 68 words: 64 payload words plus
-//      copies of the next row's first four, so any 4-word window read stays
-//      in one row, rows start 16-byte aligned, and lanes whose sub-streams
-//      start ~50 words apart spread over the LDS banks instead of falling on
-//      a few;
-//   2. per lane and per 8 symbols: fetch 4 words at the current bit, funnel
-//      them into a 96-bit window (>= 96 valid bits), then 8 times: read the
-//      16-bit table entry ((19 - length) | symbol << 8) of the 12 bits at the
-//      current position, take the next entry's offset from the unadvanced
-//      window shifted by the entry, and advance the window with funnel
-//      shifts (v_alignbit) by the entry + 13;
-//   3. every 128 decoded bytes of a lane go out as eight adjacent 16-byte
-//      stores (whole 128-byte lines);
+//   1. the staged span sits in LDS as contiguous words (a span starts on a
+//      64-word boundary);
+//   2. per lane and per 8 symbols: fetch 4 words around the current bit,
+//      funnel them into a 96-bit window (>= 96 valid bits), then 8 times:
+//      read the 32-bit table entry ((18 - length) | symbol << 8) of the 12
+//      bits at the current position, take the next entry's offset from the
+//      unadvanced window shifted by the entry, and advance the window with
+//      funnel shifts (v_alignbit) by the entry + 14 (lut32_step8);
+//   3. once the group is decoded, its output goes out through the free
+//      staging rows, half a sub-stream at a time, so that every store
+//      instruction writes whole 128-byte lines (store_group);
 //   4. the sub-stream must end exactly at the next sub-stream's first bit (or
 //      at chunk_bits); any mismatch sets *status = PC_ERR_CORRUPT.
-// A group whose span does not fit the LDS budget, and a last group that is
-// not full, are leftovers: after its staged groups, each workgroup decodes
-// its share of them straight from global memory (only data that barely
-// compresses produces unstaged groups).  The QLC variant replaces the 12-bit
+// A group whose span does not fit the LDS budget (above 7.9 bits per symbol:
+// data the code does not fit), and a last group that is not full, are
+// leftovers: after its staged groups, each workgroup decodes its share of
+// them straight from global memory.  The QLC variant replaces the 12-bit
 // table with the page's own decoder: a 3-bit area number, that area's
 // fixed-width index, and the 256-entry rank -> symbol table.  Its per-area
 // widths and first ranks sit in registers (looked up with v_perm), so the
@@ -45,35 +43,49 @@ namespace pc {
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint32_t kRow = 64;     // payload words per LDS row
-constexpr uint32_t kRowPad = 68;  // row + copies of the next row's first 4 words
-// Staged span: up to 16512 words of payload, enough for a group at 8 bits
-// per symbol (16384 words) from a row-aligned start (17 x 16 B per lane in
-// flight), with two workgroups in a CU's LDS.
-constexpr uint32_t kPrefetch = 17;
-constexpr uint32_t kMaxStageWords = kPrefetch * 4 * kThreads;  // 17408
-constexpr uint32_t kStageRows = 258;
-static_assert(kStageRows * kRow <= kMaxStageWords, "prefetch covers the staged span");
+constexpr uint32_t kRow = 64;  // a staged span starts on a multiple of 64 words
+// Staged span: up to 16256 words of payload, a group at 7.9 bits per symbol
+// from a 64-word-aligned start (16 x 16 B per lane in flight), plus 4 spare
+// words for the window reads at its end, beside the 16 KiB table, with two
+// workgroups in a CU's LDS.
+constexpr uint32_t kLutBytes = 16384;
+constexpr uint32_t kPrefetch = 16;
+constexpr uint32_t kStageWords = 16256;
+constexpr uint32_t kStageBytes = (kStageWords + 4) * 4;
 constexpr uint32_t kGroupsPerCU = 2;
+static_assert(kStageWords <= kPrefetch * 4 * kThreads, "prefetch covers the staged span");
+// static LDS: the tables and the leftover list (below)
+static_assert(2 * (kLutBytes + 272 + kStageBytes) <= 160 * 1024, "two workgroups per CU");
 
 __device__ __forceinline__ void flag_corrupt(uint32_t *status) {
     atomicCAS(status, 0u, (uint32_t)PC_ERR_CORRUPT);
 }
 
-__device__ __forceinline__ uint32_t row_index(uint32_t a) { return a + 4 * (a >> 6); }
-
 // Payload word sources.  Indices are clamped so that corrupt positions never
-// read outside the staged words or the payload.
+// read outside the staged words or the payload.  fetch4 reads words a .. a+3;
+// fetch4m reads words q-1 .. q+2 (the window of the table decoder, see
+// lut32_step8; word -1 of the staged span is the LDS word before it, read but
+// never used, as are words past the span).
 struct LdsWords {
     const uint32_t *w;
     uint32_t last;  // last staged word (relative)
     __device__ __forceinline__ void fetch4(uint32_t a, uint32_t (&v)[4]) const {
         a = a < last ? a : last;
-        const uint32_t i = row_index(a);
-        v[0] = w[i];
-        v[1] = w[i + 1];
-        v[2] = w[i + 2];
-        v[3] = w[i + 3];
+        v[0] = w[a];
+        v[1] = w[a + 1];
+        v[2] = w[a + 2];
+        v[3] = w[a + 3];
+    }
+    __device__ __forceinline__ void fetch4m(uint32_t q, uint32_t (&v)[4]) const {
+        // q = last + 1 is a lane whose remaining bits all lie in the last
+        // word (read as word q - 1); the spare words after the span keep the
+        // reads of q .. q + 2 inside the allocation
+        q = q <= last ? q : last + 1;
+        const uint32_t *p = w + q - 1;
+        v[0] = p[0];
+        v[1] = p[1];
+        v[2] = p[2];
+        v[3] = p[3];
     }
 };
 
@@ -84,10 +96,15 @@ struct GlobalWords {
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] = w[(uint64_t)a + k < last ? (uint64_t)a + k : last];
     }
+    __device__ __forceinline__ void fetch4m(uint32_t q, uint32_t (&v)[4]) const {
+        const uint64_t a = (uint64_t)q - 1;  // wraps for q = 0: clamped, and then unused
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = w[a + k < last ? a + k : last];
+    }
 };
 
 struct Tables {
-    const uint16_t *lut;  // LDS: 4096 x ((19 - length) | symbol << 8), 0 = no codeword
+    const uint32_t *lut;  // LDS: 4096 x ((18 - length) | symbol << 8), 0 = no codeword
     const uint8_t *sym;   // LDS (QLC mode): symbol of rank r for r < 256, 0 up to 1023
     // QLC mode, one byte per area a (a = 0..3 in *_lo, 4..7 in *_hi), read
     // with v_perm, so that no table on the decoding chain sits in memory:
@@ -102,63 +119,99 @@ struct Tables {
     bool qlc_check;
 };
 
-// Whether a sub-stream met a bit pattern that is no codeword: LUT mode ORs
-// the entries' invalid flags, QLC mode keeps the largest window seen.
+// Whether a sub-stream met a bit pattern that is no codeword: LUT mode keeps
+// the least table entry read (a codeword's entry is at least 6, "no
+// codeword" is 0), QLC mode the largest window seen.
+template <int MODE>
+__device__ __forceinline__ uint32_t no_invalid_yet() { return MODE == kDecodeLut12 ? ~0u : 0u; }
+
 template <int MODE>
 __device__ __forceinline__ bool saw_invalid(uint32_t bad, const Tables &t) {
-    return MODE == kDecodeLut12 ? bad != 0 : (t.qlc_check && bad >= t.qlc_lim);
+    return MODE == kDecodeLut12 ? bad == 0 : (t.qlc_check && bad >= t.qlc_lim);
 }
 
-// Decode 8 symbols from the 96-bit window (h, m, l); returns them packed
-// little-endian in two words and adds the bits consumed to pos.  Symbols at
-// index >= lim (masked variant only) consume nothing.
-//
-// Entries are (19 - length) | symbol << 8 in LUT mode; QLC mode keeps
-// 32 - length and the symbol in two registers.  In LUT mode the
-// byte offset of the next entry is taken from the window before it is
-// advanced: the 12 bits after a codeword of length len start len bits into
-// h, so (h >> (19 - len)) & 0x1FFE is twice their value, and v_lshrrev reads
-// exactly the 5 low bits of the entry as its count.  The window advance
-// (funnel shifts by 32 - len = entry + 13 in the low 5 bits) then runs
-// beside the next table read instead of before it: per symbol the chain of
-// dependent instructions is one LDS read, one shift and one mask.  (The
-// window has >= 96 valid bits and 7 codewords take <= 84, so the 12 bits
-// after any of the first 7 are valid.)
-template <int MODE, bool MASKED, bool CHECK>
-__device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint32_t &pos, uint32_t &bad,
-                                        const Tables &t, uint32_t k0, uint32_t lim, uint32_t &o0, uint32_t &o1) {
-    uint32_t e[8], y[8];  // y: the symbols (QLC mode)
-    uint32_t a = (h >> (31 - kPeek)) & 0x1FFE;  // byte offset of the first entry (LUT mode)
+// Table decoder with one 32-bit entry per 12-bit peek: (18 - length) in the
+// low 5 bits (0 = no codeword), the symbol in byte 1.  The next entry's byte
+// offset comes from the window before it is advanced: the 12 bits after a
+// codeword of length len start len bits into h, so (h >> (18 - len)) &
+// 0x3FFC is four times their value; the window's funnel shifts (by 32 - len
+// = entry + 14 in the low 5 bits) run beside the next table read.  Per
+// symbol the chain of dependent instructions is one LDS read, one shift and
+// one mask (32-bit LDS reads of random entries also run at about twice the
+// rate of 16-bit ones, measured).  The bit position is kept negated (npos =
+// -pos, mod 2^32): the window is the 96 bits from pos, funnelled from the
+// words q-1 .. q+2 with q = (pos + 31) / 32 by v_alignbit with shift npos (its
+// low 5 bits are (32 - pos % 32) % 32; pos % 32 == 0 shifts by 0 and takes
+// word q itself).  (96 valid bits, and 7 codewords take <= 84, so the 12
+// bits after any of the first 7 are valid.)  Symbols at index >= lim (masked
+// variant only) consume nothing.  Returns the 8 symbols packed little-endian
+// in o0, o1.
+template <bool MASKED, bool CHECK, class Src>
+__device__ __forceinline__ void lut32_step8(const Src &src, uint32_t &npos, uint32_t &bad, const uint32_t *lut,
+                                            uint32_t k0, uint32_t lim, uint32_t &o0, uint32_t &o1) {
+    uint32_t w[4];
+    src.fetch4m((31u - npos) >> 5, w);
+    uint32_t h = __builtin_amdgcn_alignbit(w[0], w[1], npos);
+    uint32_t m = __builtin_amdgcn_alignbit(w[1], w[2], npos);
+    uint32_t l = __builtin_amdgcn_alignbit(w[2], w[3], npos);
+    uint32_t a = (h >> 18) & 0x3FFC;
+    uint32_t e[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        uint32_t ek, inv, sh;  // sh: 32 - length in the 5 bits v_alignbit reads
+        const bool masked = MASKED && k0 + k >= lim;
+        uint32_t ek = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(lut) + a);
+        if (CHECK) {
+            const uint32_t c = masked ? ~0u : ek;
+            bad = bad < c ? bad : c;
+        }
+        if (masked) ek = (ek & 0xFF00u) | 18u;  // length 0: the window is kept
+        if (k < 7) a = (h >> (ek & 31)) & 0x3FFC;
+        const uint32_t s = ek + 14;  // 32 - length in the low 5 bits (32: masked, no advance)
+        if (k < 7) {
+            const uint32_t h2 = __builtin_amdgcn_alignbit(h, m, s);
+            const uint32_t m2 = __builtin_amdgcn_alignbit(m, l, s);
+            const uint32_t l2 = __builtin_amdgcn_alignbit(l, 0u, s);
+            if (!masked) {
+                h = h2;
+                m = m2;
+                l = l2;
+            }
+        }
+        e[k] = ek;
+    }
+    // each low byte is 18 - length (<= 17): four of them sum below 256
+    const uint32_t s0 = (e[0] + e[1] + e[2] + e[3]) & 0xFF, s1 = (e[4] + e[5] + e[6] + e[7]) & 0xFF;
+    npos += s0 + s1 - 8 * 18;  // -(bits consumed); masked entries count 18, i.e. nothing
+    o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
+    o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
+    // pack and check here: left to the scheduler, the packing sinks towards
+    // the store and the checks towards the end of the stream, and both keep
+    // all eight entries of every step alive until then
+    asm volatile("" : "+v"(o0), "+v"(o1));
+    if (CHECK) asm volatile("" : "+v"(bad));
+}
+
+// QLC decoder, 8 symbols from the 96-bit window (h, m, l); returns them
+// packed little-endian in two words and adds the bits consumed to pos.
+// Symbols at index >= lim (masked variant only) consume nothing.
+template <bool MASKED, bool CHECK>
+__device__ __forceinline__ void qlc_step8(uint32_t h, uint32_t m, uint32_t l, uint32_t &pos, uint32_t &bad,
+                                          const Tables &t, uint32_t k0, uint32_t lim, uint32_t &o0, uint32_t &o1) {
+    uint32_t e[8], y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
         const bool masked = MASKED && k0 + k >= lim;  // length 0: the window is kept
-        if (MODE == kDecodeLut12) {
-            ek = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(t.lut) + a);
-            inv = (ek & 0xFF) == 0;
-            if (masked) ek = (ek & 0xFF00) | 19;
-            if (k < 7) a = (h >> (ek & 31)) & 0x1FFE;
-            sh = ek + 13;
-        } else {
-            // the area number (3 bits) selects bytes of the area registers
-            // (the other selector bytes, 0x0C, give zeros; one funnel shift
-            // forms the selector: (0x01818180 << 3) | (h >> 29)); the chain
-            // per symbol is funnel shift, v_perm, funnel shift, with the
-            // rank and the symbol read beside it (a rank past 255 reads a
-            // zero of the 1 KiB table)
-            const uint32_t sel = __builtin_amdgcn_alignbit(0x01818180u, h, 29);
-            sh = __builtin_amdgcn_perm(t.sh_hi, t.sh_lo, sel);
-            const uint32_t bw = __builtin_amdgcn_perm(t.bw_hi, t.bw_lo, sel);
-            const uint32_t r = __builtin_amdgcn_perm(t.st_hi, t.st_lo, sel) + __builtin_amdgcn_ubfe(h, sh, bw);
-            if (CHECK && !masked) bad = bad > h ? bad : h;
-            ek = masked ? 32u : sh;
-            y[k] = t.sym[r];
-            inv = 0;
-        }
-        if (MODE == kDecodeLut12) {
-            if (masked) inv = 0;
-            if (CHECK) bad |= inv;
-        }
+        // the area number (3 bits) selects bytes of the area registers (the
+        // other selector bytes, 0x0C, give zeros; one funnel shift forms the
+        // selector: (0x01818180 << 3) | (h >> 29)); the chain per symbol is
+        // funnel shift, v_perm, funnel shift, with the rank and the symbol
+        // read beside it (a rank past 255 reads a zero of the 1 KiB table)
+        const uint32_t sel = __builtin_amdgcn_alignbit(0x01818180u, h, 29);
+        const uint32_t sh = __builtin_amdgcn_perm(t.sh_hi, t.sh_lo, sel);  // 32 - length
+        const uint32_t bw = __builtin_amdgcn_perm(t.bw_hi, t.bw_lo, sel);
+        const uint32_t r = __builtin_amdgcn_perm(t.st_hi, t.st_lo, sel) + __builtin_amdgcn_ubfe(h, sh, bw);
+        if (CHECK && !masked) bad = bad > h ? bad : h;
+        y[k] = t.sym[r];
         const uint32_t h2 = __builtin_amdgcn_alignbit(h, m, sh);
         const uint32_t m2 = __builtin_amdgcn_alignbit(m, l, sh);
         const uint32_t l2 = __builtin_amdgcn_alignbit(l, 0u, sh);
@@ -167,26 +220,36 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
             m = m2;
             l = l2;
         }
-        e[k] = ek;
+        e[k] = masked ? 32u : sh;
     }
-    if (MODE == kDecodeLut12) {
-        // each low byte is 19 - length: 4 of them sum below 256
-        const uint32_t s0 = (e[0] + e[1] + e[2] + e[3]) & 0xFF, s1 = (e[4] + e[5] + e[6] + e[7]) & 0xFF;
-        pos += 8 * 19 - s0 - s1;
-        o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
-        o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
-    } else {
-        // e[k] = 32 - length (<= 32 each)
-        pos += 8 * 32 - (e[0] + e[1] + e[2] + e[3]) - (e[4] + e[5] + e[6] + e[7]);
-        o0 = __builtin_amdgcn_perm(y[1], y[0], 0x0C0C0400u) | __builtin_amdgcn_perm(y[3], y[2], 0x04000C0Cu);
-        o1 = __builtin_amdgcn_perm(y[5], y[4], 0x0C0C0400u) | __builtin_amdgcn_perm(y[7], y[6], 0x04000C0Cu);
-    }
-    // pack and check here: left to the scheduler, the packing sinks towards
-    // the store and the checks towards the end of the stream, and both keep
-    // all eight entries of every step alive until then
+    // e[k] = 32 - length (<= 32 each)
+    pos += 8 * 32 - (e[0] + e[1] + e[2] + e[3]) - (e[4] + e[5] + e[6] + e[7]);
+    o0 = __builtin_amdgcn_perm(y[1], y[0], 0x0C0C0400u) | __builtin_amdgcn_perm(y[3], y[2], 0x04000C0Cu);
+    o1 = __builtin_amdgcn_perm(y[5], y[4], 0x0C0C0400u) | __builtin_amdgcn_perm(y[7], y[6], 0x04000C0Cu);
     asm volatile("" : "+v"(o0), "+v"(o1));
     if (CHECK) asm volatile("" : "+v"(bad));
 }
+
+// 8 symbols of either decoder from the current position.
+template <int MODE, bool MASKED, bool CHECK, class Src>
+__device__ __forceinline__ void step8(const Src &src, uint32_t &pos, uint32_t &bad, const Tables &t, uint32_t k0,
+                                      uint32_t lim, uint32_t &o0, uint32_t &o1) {
+    if (MODE == kDecodeLut12) {  // pos holds -position here
+        lut32_step8<MASKED, CHECK>(src, pos, bad, t.lut, k0, lim, o0, o1);
+    } else {
+        uint32_t w[4];
+        src.fetch4(pos >> 5, w);
+        const uint32_t sh = pos & 31;
+        const uint32_t h = (uint32_t)(((((uint64_t)w[0] << 32) | w[1]) << sh) >> 32);
+        const uint32_t m = (uint32_t)(((((uint64_t)w[1] << 32) | w[2]) << sh) >> 32);
+        const uint32_t l = (uint32_t)(((((uint64_t)w[2] << 32) | w[3]) << sh) >> 32);
+        qlc_step8<MASKED, CHECK>(h, m, l, pos, bad, t, k0, lim, o0, o1);
+    }
+}
+
+// Positions as the steps keep them: negated in LUT mode.
+template <int MODE>
+__device__ __forceinline__ uint32_t to_step_pos(uint32_t pos) { return MODE == kDecodeLut12 ? 0u - pos : pos; }
 
 // Masked decode (the leftover groups): symbols [s_begin, s_end) of one
 // sub-stream in blocks of 16; a lane writes only its bytes below lim (lanes
@@ -194,19 +257,13 @@ __device__ __forceinline__ void decode8(uint32_t h, uint32_t m, uint32_t l, uint
 template <int MODE, class Src>
 __device__ __forceinline__ uint32_t decode_masked(const Src &src, uint32_t pos, uint32_t lim, const Tables &t,
                                                   uint8_t *dst, uint32_t &bad, uint32_t s_begin, uint32_t s_end) {
+    pos = to_step_pos<MODE>(pos);
 #pragma unroll 1
     for (uint32_t base = s_begin; base < s_end; base += 16) {
         uint32_t o[4];
 #pragma unroll
-        for (uint32_t q = 0; q < 2; ++q) {
-            uint32_t w[4];
-            src.fetch4(pos >> 5, w);
-            const uint32_t sh = pos & 31;
-            const uint32_t h = (uint32_t)(((((uint64_t)w[0] << 32) | w[1]) << sh) >> 32);
-            const uint32_t m = (uint32_t)(((((uint64_t)w[1] << 32) | w[2]) << sh) >> 32);
-            const uint32_t l = (uint32_t)(((((uint64_t)w[2] << 32) | w[3]) << sh) >> 32);
-            decode8<MODE, true, true>(h, m, l, pos, bad, t, base + q * 8, lim, o[2 * q], o[2 * q + 1]);
-        }
+        for (uint32_t q = 0; q < 2; ++q)
+            step8<MODE, true, true>(src, pos, bad, t, base + q * 8, lim, o[2 * q], o[2 * q + 1]);
         if (base + 16 <= lim) {
             *reinterpret_cast<uint4 *>(dst + base) = make_uint4(o[0], o[1], o[2], o[3]);
         } else {
@@ -217,7 +274,7 @@ __device__ __forceinline__ uint32_t decode_masked(const Src &src, uint32_t pos, 
                     if (base + 4 * q + k < lim) dst[base + 4 * q + k] = (uint8_t)(o[q] >> (8 * k));
         }
     }
-    return pos;
+    return to_step_pos<MODE>(pos);
 }
 
 // Loaded values pass through pin() where they are first needed: the empty
@@ -236,9 +293,8 @@ __device__ __forceinline__ uint32_t vgpr_copy(uint32_t v) {
 }
 
 // Half a sub-stream (128 symbols) of a lane whose 256 symbols all lie in
-// [0, n), decoded into registers and then stored as one 128-byte line per
-// lane (eight adjacent 16-byte stores: the L2 receives whole lines, not
-// 16-byte pieces that other stores complete much later).
+// [0, n), decoded into registers (stored with the other half once the group
+// is decoded, see store_group).
 constexpr uint32_t kHalf = kSub / 2;
 constexpr uint32_t kHalfWords = kHalf / 4;
 
@@ -249,26 +305,41 @@ constexpr uint32_t kHalfWords = kHalf / 4;
 template <int MODE, bool CHECK, class Side>
 __device__ __forceinline__ uint32_t decode_half(const LdsWords &src, uint32_t pos, const Tables &t, uint32_t &bad,
                                                 uint32_t (&o)[kHalfWords], Side &&side) {
+    pos = to_step_pos<MODE>(pos);
 #pragma unroll
     for (uint32_t q = 0; q < kHalf / 8; ++q) {
-        uint32_t w[4];
-        src.fetch4(pos >> 5, w);
-        const uint32_t sh = pos & 31;
-        const uint32_t h = (uint32_t)(((((uint64_t)w[0] << 32) | w[1]) << sh) >> 32);
-        const uint32_t m = (uint32_t)(((((uint64_t)w[1] << 32) | w[2]) << sh) >> 32);
-        const uint32_t l = (uint32_t)(((((uint64_t)w[2] << 32) | w[3]) << sh) >> 32);
-        decode8<MODE, false, CHECK>(h, m, l, pos, bad, t, 0, kHalf, o[2 * q], o[2 * q + 1]);
+        step8<MODE, false, CHECK>(src, pos, bad, t, 0, kHalf, o[2 * q], o[2 * q + 1]);
         side(q);
         asm volatile("" ::: "memory");  // the side work stays at this step
     }
-    return pos;
+    return to_step_pos<MODE>(pos);
 }
 
-__device__ __forceinline__ void store_half(uint8_t *dst, const uint32_t (&o)[kHalfWords]) {
-    uint4 *d = reinterpret_cast<uint4 *>(dst);
+// A group's output goes out through LDS, half a sub-stream (128 bytes per
+// lane) at a time: each wave writes its lanes' 8 quads into its own 8 KiB
+// of the free staging rows, then reads them back so that every store
+// instruction writes eight whole 128-byte lines (8 lanes per line) instead of
+// 16 bytes into each of 64 lines.  Quad q of lane l sits at slot
+// l * 8 + (q ^ (l % 8)).
+__device__ __forceinline__ void store_group(uint4 *buf, uint8_t *out, uint32_t tid, const uint32_t (&o1)[kHalfWords],
+                                            const uint32_t (&o2)[kHalfWords]) {
+    const uint32_t w = tid >> 6, l = tid & 63;
+    uint4 *wb = buf + w * 512;
+    uint8_t *wout = out + (size_t)w * 64 * kSub;
 #pragma unroll
-    for (uint32_t k = 0; k < kHalfWords / 4; ++k)
-        d[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+    for (uint32_t h = 0; h < 2; ++h) {
+        const uint32_t *o = h ? o2 : o1;
+        if (h) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the first half's reads are done
+#pragma unroll
+        for (uint32_t q = 0; q < 8; ++q)
+            wb[l * 8 + (q ^ (l & 7))] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's own writes, read by its other lanes
+#pragma unroll
+        for (uint32_t t = 0; t < 8; ++t) {
+            const uint32_t L = 8 * t + (l >> 3), Q = l & 7;
+            *reinterpret_cast<uint4 *>(wout + L * kSub + h * kHalf + Q * 16) = wb[L * 8 + (Q ^ (L & 7))];
+        }
+    }
 }
 
 // Container entries a lane depends on (loaded one group ahead).
@@ -403,7 +474,7 @@ __device__ __forceinline__ uint64_t last_quad(uint64_t lo, uint64_t hi, uint64_t
 __device__ __forceinline__ void prefetch_quad(Prefetch &pf, uint32_t k, gquad *payload, uint64_t lo,
                                               uint64_t q_last, uint32_t tid) {
     const uint64_t q = (lo & ~(uint64_t)(kRow - 1)) / 4 + tid + k * kThreads;
-    const u32x4 v = __builtin_nontemporal_load(payload + (q < q_last ? q : q_last));
+    const u32x4 v = payload[q < q_last ? q : q_last];
     pf.q[k] = make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -417,12 +488,12 @@ __device__ __forceinline__ void issue_prefetch(Prefetch &pf, gquad *payload, uin
 template <int MODE>
 __device__ __forceinline__ void load_tables(const uint8_t *cbb, uint4 *tab4, uint32_t tid) {
     if (MODE == kDecodeLut12) {
-        // 16-bit entries (19 - length) | symbol << 8 (0: no codeword)
+        // 32-bit entries (18 - length) | symbol << 8 (0: no codeword)
         const uint8_t *ds = cbb + kOffDecSym, *dl = cbb + kOffDecSym + 4096;
-        uint16_t *lut = reinterpret_cast<uint16_t *>(tab4);
+        uint32_t *lut = reinterpret_cast<uint32_t *>(tab4);
         for (uint32_t i = tid; i < 4096; i += kThreads) {
             const uint32_t len = dl[i];
-            lut[i] = (uint16_t)(len ? ((19 - len) | ((uint32_t)ds[i] << 8)) : 0u);
+            lut[i] = len ? ((18 - len) | ((uint32_t)ds[i] << 8)) : 0u;
         }
     } else {
         // symbol of rank r, then zeros up to rank 1023 (a rank is below
@@ -541,11 +612,7 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
 #pragma unroll
             for (uint32_t k = 0; k < kPrefetch; ++k) {
                 const uint32_t q = tid + k * kThreads;
-                if (q < nq && q < full_q) {
-                    const uint32_t i = row_index(4 * q);  // a multiple of 4
-                    stage4[i / 4] = pf.q[k];
-                    if ((q & 15) == 0 && q) stage4[i / 4 - 1] = pf.q[k];  // copies ending the previous row
-                }
+                if (q < nq && q < full_q) stage4[q] = pf.q[k];
             }
             if (nq > full_q && tid == (uint32_t)full_q % kThreads) {
                 // the span reaches the payload's last quad, which may be
@@ -556,10 +623,7 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
                     const uint64_t i = wbase + 4 * full_q + w;
                     v[w] = i < payload_words ? payload[i] : 0u;
                 }
-                const uint32_t i = row_index(4 * (uint32_t)full_q);
-                const uint4 qv = make_uint4(v[0], v[1], v[2], v[3]);
-                stage4[i / 4] = qv;
-                if ((full_q & 15) == 0 && full_q) stage4[i / 4 - 1] = qv;
+                stage4[full_q] = make_uint4(v[0], v[1], v[2], v[3]);
             }
         }
         __syncthreads();
@@ -580,22 +644,19 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
         nq_last = more ? last_quad(nlo, nhi, payload_words) : 0;
         nq_lo = more ? nlo : 0;
         const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
-        uint8_t *dst = out + (grp * kThreads + tid) * kSub;
         const LdsWords src{stage, (uint32_t)((cnt < stage_cap ? cnt : stage_cap) - (cnt > 0 ? 1 : 0))};
-        uint32_t bad = 0;
+        uint32_t bad = no_invalid_yet<MODE>();
         // first half: the next group's payload loads, two per step from step
         // 0 (its span entries were loaded one group ahead)
         uint32_t pos = decode_half<MODE, CHECK>(src, job.pos0, t, bad, o1, [&](uint32_t q) {
             if (2 * q < kPrefetch) prefetch_quad(pf, 2 * q, pq, nq_lo, nq_last, tid);
             if (2 * q + 1 < kPrefetch) prefetch_quad(pf, 2 * q + 1, pq, nq_lo, nq_last, tid);
         });
-        // second half: the first half's 128 bytes, 16 per step
-        if (staged) store_half(dst, o1);
         pos = decode_half<MODE, CHECK>(src, pos, t, bad, o2, [&](uint32_t q) {});
-        if (staged) {
-            if (job.ok && (saw_invalid<MODE>(bad, t) || pos != job.pos_want)) flag_corrupt(status);
-            store_half(dst + kHalf, o2);
-        }
+        if (staged && job.ok && (saw_invalid<MODE>(bad, t) || pos != job.pos_want)) flag_corrupt(status);
+        // the staging rows take the output once every lane is done with them
+        __syncthreads();
+        if (staged) store_group(stage4, out + grp * kThreads * kSub, tid, o1, o2);
 
         if (!more) break;
         grp = nxt;
@@ -657,7 +718,7 @@ __device__ __forceinline__ void decode_batch(const Leftovers &lo_, uint32_t nt, 
         if (payload_words <= wbase) continue;  // nothing readable: every lane was flagged
         uint8_t *dst = out + (grp * kThreads + tid) * kSub;
         GlobalWords src{payload + wbase, payload_words - wbase - 1};
-        uint32_t bad = 0;
+        uint32_t bad = no_invalid_yet<MODE>();
         const uint32_t pos_end = decode_masked<MODE>(src, job.pos0, job.lim, t, dst, bad, 0, kSub);
         if (job.ok && (saw_invalid<MODE>(bad, t) || pos_end != job.pos_want)) flag_corrupt(status);
     }
@@ -679,7 +740,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     uint32_t stage_cap) {
     // Tables at fixed LDS addresses (folded into the instructions' offset
     // fields); the payload staging rows are the dynamic part.
-    __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 64];
+    __shared__ uint4 tab4[MODE == kDecodeLut12 ? kLutBytes / 16 : 64];
     __shared__ Leftovers left;
     extern __shared__ uint4 stage4[];
     uint32_t *stage = reinterpret_cast<uint32_t *>(stage4);
@@ -689,7 +750,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     load_tables<MODE>(cbb, tab4, tid);
     const bool kind_ok = MODE == kDecodeLut12 || cbp->kind == PC_CODEBOOK_QLC;
     Tables t;
-    t.lut = reinterpret_cast<const uint16_t *>(tab4);
+    t.lut = reinterpret_cast<const uint32_t *>(tab4);
     t.sym = reinterpret_cast<const uint8_t *>(tab4);
     if (MODE == kDecodeQlc) qlc_area_regs(cbb, t);
 
@@ -727,7 +788,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     const uint32_t *__restrict__ sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub, uint64_t num_groups,
     uint64_t num_full, uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status,
     uint32_t stage_cap) {
-    __shared__ uint4 tab4[MODE == kDecodeLut12 ? 512 : 64];
+    __shared__ uint4 tab4[MODE == kDecodeLut12 ? kLutBytes / 16 : 64];
     __shared__ Leftovers left;
     const uint32_t tid = threadIdx.x;
     const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
@@ -735,7 +796,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     bool loaded = false;
     const bool kind_ok = MODE == kDecodeLut12 || cbp->kind == PC_CODEBOOK_QLC;
     Tables t;
-    t.lut = reinterpret_cast<const uint16_t *>(tab4);
+    t.lut = reinterpret_cast<const uint32_t *>(tab4);
     t.sym = reinterpret_cast<const uint8_t *>(tab4);
     if (MODE == kDecodeQlc) qlc_area_regs(cbb, t);
     const uint64_t G = gridDim.x;
@@ -764,10 +825,9 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     const uint64_t num_sub = (nc - 1) * (chunk / kSub) + (last + kSub - 1) / kSub;
     const uint64_t num_groups = (num_sub + kThreads - 1) / kThreads;
     // LDS budget for a staged span: two workgroups share a CU's 160 KiB:
-    // 258 rows of 68 words beside the 8 KiB table, i.e. up to 16512 payload
-    // words (8 bits per symbol from a row-aligned start).
-    const uint64_t cap = kStageRows * kRow;
-    const size_t shmem = kStageRows * kRowPad * 4;
+    // kStageWords words (+ 4 spare) beside the 8 KiB of tables.
+    const uint64_t cap = kStageWords;
+    const size_t shmem = kStageBytes;
     // Per device (the current one), set once: its CU count, and the
     // dynamic-LDS limit of the main kernels.  Concurrent first calls may
     // both query and set; they store the same values.
@@ -787,7 +847,7 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     const void *fn = mode == kDecodeLut12 ? (const void *)decode_kernel<kDecodeLut12>
                                           : (const void *)decode_kernel<kDecodeQlc>;
     if (!attr_of[dev][mode].load(std::memory_order_relaxed)) {
-        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kStageRows * kRowPad * 4);
+        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kStageBytes);
         if (e != hipSuccess) return e;
         attr_of[dev][mode].store(true, std::memory_order_relaxed);
     }

@@ -32,3 +32,19 @@ def test_ms_stats():
     st = bench.ms_stats([1.0, 2.0, 3.0, 4.0, 5.0])
     assert st["mean"] == 3.0 and st["median"] == 3.0 and st["min"] == 1.0 and st["max"] == 5.0
     assert st["p10"] == 1.4 and st["p90"] == 4.6
+
+
+def test_oracle_parity_leg_on_oracle_streams():
+    """The per-configuration oracle comparison of the cpu_baseline leg, fed the
+    oracle's own stream (every array must compare equal), and one that has a
+    flipped payload bit (the payload must compare unequal)."""
+    x = W.make("normal_1m", 0)[: 5 * 4096 + 77]
+    counts = np.bincount(W.make("normal_1m", 1), minlength=256)
+    book = cb.codebook([int(c) for c in counts], "huffman", None)
+    s = coder.encode(x, book["lengths"], book["codes"], 4096, threads=2)
+    host = {k: s[k].copy() for k in ("payload", "chunk_bits", "chunk_word_offset", "sub_off")}
+    got = bench.oracle_parity((x, counts, "huffman", None, 4096, host), 2)
+    assert all(got.values()), got
+    host["payload"][3] ^= 1
+    got = bench.oracle_parity((x, counts, "huffman", None, 4096, host), 2)
+    assert not got["payload"] and got["chunk_bits"] and got["oracle_round_trip"]
