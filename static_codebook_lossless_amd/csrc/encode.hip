@@ -498,19 +498,282 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
     }
 }
 
+// ---------------------------------------------------------------------------
+// Units of 64 KiB (1, 2 or 4 whole chunks of 64, 32 or 16 KiB), persistent
+// 512-lane workgroups, two per CU (128 registers per lane).  A unit is eight
+// tiles of 8 KiB; lane l of tile r owns its 16 symbols at r * 8192 + 16 l.
+//   phase 1: all eight tiles are already in registers (loaded during the
+//     previous unit); each tile's 16 (code, length) lookups become four
+//     groups of <= 48 bits, kept in registers, and a wave scan of the bit
+//     counts.  One barrier, then one wave scan over the 64 (tile, wave)
+//     totals gives every lane's bit offset in every tile, the chunks' bit
+//     counts and the unit's word count, which is published at once.
+//   phase 2: the groups are ORed into the LDS buffer at their offsets, with
+//     no barrier, and each tile's registers then take the next unit's input
+//     (its ticket was taken at the end of phase 1), so the loads of one unit
+//     are in flight while the next is packed.  Wave 0 then walks back over
+//     the earlier units' descriptors; as every unit publishes its count
+//     before it packs, the walk mostly finds its predecessors published.
+//   the unit is stored once, coalesced, at its final offset.
+// A unit whose words would not fit the buffer (only data that does not
+// compress) does its look-back first and is placed and stored in two halves
+// of four tiles from the same registers.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kUT = 512;                  // lanes
+constexpr uint32_t kUW = kUT / 64;             // waves
+constexpr uint32_t kUTiles = 8;                // tiles per unit
+constexpr uint32_t kUTile = kUT * kSymPerLane; // 8192 symbols
+constexpr uint32_t kUBufW = 16392;             // a unit at 8 bits per symbol, chunk padding and the fit margin
+
+struct UnitShared {
+    uint32_t tab[256];                 // code << 16 | length
+    uint32_t wtot[kUTiles * kUW];      // per (tile, wave): bits
+    uint32_t misc[4];                  // [0] ticket of this unit, [1] of the next, [2..3] its word offset
+    uint32_t buf[kUBufW + 8];
+};
+
+// One lane's groups of one tile: two groups of <= 48 bits in three words (the
+// high 16 bits of both in the third), and the four group lengths in bytes.
+struct TileGroups {
+    uint32_t w[6];
+    uint32_t n;
+};
+
+__device__ __forceinline__ void keep_groups(const uint64_t (&g)[4], const uint32_t (&ng)[4], TileGroups &tg) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        tg.w[3 * h] = (uint32_t)g[2 * h];
+        tg.w[3 * h + 1] = (uint32_t)g[2 * h + 1];
+        tg.w[3 * h + 2] = (uint32_t)(g[2 * h] >> 32) | (uint32_t)(g[2 * h + 1] >> 32) << 16;
+    }
+    tg.n = ng[0] | ng[1] << 8 | ng[2] << 16 | ng[3] << 24;
+    // the packed words are what stays live (the compiler would otherwise
+    // keep the 64-bit groups and the unpacked counts instead)
+#pragma unroll
+    for (int i = 0; i < 6; ++i) asm volatile("" : "+v"(tg.w[i]));
+    asm volatile("" : "+v"(tg.n));
+}
+
+__device__ __forceinline__ void place_tile(const TileGroups &tg, uint32_t p, uint32_t *buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t h = q >> 1;
+        const uint32_t hi = (q & 1) ? tg.w[3 * h + 2] >> 16 : tg.w[3 * h + 2] & 0xFFFF;
+        const uint64_t g = ((uint64_t)hi << 32) | tg.w[3 * h + (q & 1)];
+        const uint32_t ng = (tg.n >> (8 * q)) & 0xFF;
+        place_group(g, ng, p, buf);
+        p += ng;
+    }
+}
+
+// The unit's look-back (one wave) and its chunks' metadata; the exclusive
+// word offset goes to sh.misc[2..3].
+template <int NC>
+__device__ __forceinline__ void unit_meta(UnitShared &sh, uint64_t *desc, uint32_t s, uint64_t words, uint32_t lane,
+                                          uint32_t max_polls, uint32_t *status, uint32_t *chunk_bits, uint64_t *cwo,
+                                          uint32_t c0, uint32_t num_chunks, const uint32_t (&cbits)[NC],
+                                          const uint32_t (&cw)[NC]) {
+    const uint64_t excl = lookback(desc, s, words, lane, max_polls, status, true);
+    if (lane == 0) {
+        sh.misc[2] = (uint32_t)excl;
+        sh.misc[3] = (uint32_t)(excl >> 32);
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            chunk_bits[c0 + k] = cbits[k];
+            cwo[c0 + k] = excl + cw[k];
+        }
+        if (c0 + NC == num_chunks) cwo[num_chunks] = excl + words;
+    }
+}
+
+__device__ __forceinline__ uint64_t unit_excl(const UnitShared &sh) {
+    return ((uint64_t)sh.misc[3] << 32) | sh.misc[2];
+}
+
+// Stores words [0, nw) of the buffer at dst (unit word fb sits at dst) and
+// clears them: after a head up to a 128-byte boundary every wave writes
+// whole lines.
+__device__ __forceinline__ void store_unit(uint32_t *buf, uint32_t *dst, uint64_t at, uint32_t nw, uint32_t tid) {
+    const uint32_t hd = (uint32_t)((32 - (at & 31)) & 31);
+    const uint32_t head = hd < nw ? hd : nw;
+    if (tid < head) {
+        __builtin_nontemporal_store(buf[tid], dst + tid);
+        buf[tid] = 0;
+    }
+    for (uint32_t i = head + tid; i < nw; i += kUT) {
+        __builtin_nontemporal_store(buf[i], dst + i);
+        buf[i] = 0;
+    }
+}
+
+template <int TPC>  // tiles per chunk: 8, 4 or 2
+__global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void encode_unit_kernel(
+    const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint32_t num_chunks, uint32_t num_units,
+    uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits, uint64_t *__restrict__ cwo,
+    uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws, uint32_t *__restrict__ status, uint32_t max_polls) {
+    constexpr int NC = kUTiles / TPC;  // chunks per unit
+    __shared__ UnitShared sh;
+    const uint32_t tid = threadIdx.x, lane = tid & 63;
+    const uint32_t wave = uniform(tid >> 6);
+    uint32_t *ticket = reinterpret_cast<uint32_t *>(ws);
+    uint64_t *desc = ws + 1;
+    if (tid == 0) sh.misc[0] = atomicAdd(ticket, 1u);
+    if (tid < 256) {
+        const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
+        sh.tab[tid] = ((uint32_t)reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid] << 16) | cbb[kOffLength + tid];
+    }
+    for (uint32_t i = tid; i < (kUBufW + 8) / 4; i += kUT) reinterpret_cast<uint4 *>(sh.buf)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    uint32_t s = uniform(sh.misc[0]);
+    uint4 x[kUTiles];
+    if (s < num_units) {
+        const uint8_t *src = in + (uint64_t)s * (kUTiles * kUTile) + tid * 16;
+#pragma unroll
+        for (uint32_t r = 0; r < kUTiles; ++r) x[r] = load_stream16(src + r * kUTile);
+    }
+    // the unit placed in the buffer last round, still to be stored
+    bool have_a = false;
+    uint32_t sa = 0, words_a = 0, cbits_a[NC], cw_a[NC];
+    while (true) {
+        const bool live = s < num_units;
+        // ---- phase 1: lookups, groups, wave scans ----------------------
+        TileGroups tg[kUTiles];
+        uint32_t ex[kUTiles];  // bits before the lane within its wave, per tile
+        if (live) {
+#pragma unroll
+            for (uint32_t r = 0; r < kUTiles; ++r) {
+                uint64_t g[4];
+                uint32_t ng[4];
+                // one tile's lookups at a time: the input passes an opaque
+                // step ordered after the previous tile's packed groups
+                // (hoisting all lookups would keep 128 results live)
+                asm volatile("" : "+v"(x[r].x), "+v"(x[r].y), "+v"(x[r].z), "+v"(x[r].w));
+                lane_groups(x[r], sh, g, ng);
+                const uint32_t bits = ng[0] + ng[1] + ng[2] + ng[3];
+                const uint32_t incl = wave_incl_scan(bits);
+                if (lane == 63) sh.wtot[r * kUW + wave] = incl;
+                ex[r] = incl - bits;
+                keep_groups(g, ng, tg[r]);
+            }
+            if (tid == 0) sh.misc[1] = atomicAdd(ticket, 1u);
+        }
+        __syncthreads();
+        // ---- offsets: a scan over the 64 (tile, wave) totals -------------
+        uint32_t s_next = 0, words = 0, exs = 0;
+        uint32_t cbase[NC], cbits[NC], cw[NC], pos[kUTiles];
+        if (live) {
+            s_next = uniform(sh.misc[1]);
+            const uint32_t v = sh.wtot[lane];
+            const uint32_t incl = wave_incl_scan(v);
+            exs = incl - v;
+            uint32_t cword = 0;
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                const int i0 = k * TPC * kUW, i1 = (k + 1) * TPC * kUW - 1;
+                cbase[k] = (uint32_t)__builtin_amdgcn_readlane((int)exs, i0);
+                cbits[k] = (uint32_t)__builtin_amdgcn_readlane((int)incl, i1) - cbase[k];
+                cw[k] = cword;
+                cword += (cbits[k] + 31) >> 5;
+            }
+            words = cword;
+            // the lane's first bit of tile r in the unit's buffer (chunk k
+            // of the unit starts on word cw[k])
+#pragma unroll
+            for (uint32_t r = 0; r < kUTiles; ++r)
+                pos[r] = cw[r / TPC] * 32 + (uint32_t)__builtin_amdgcn_readlane((int)exs, (int)(r * kUW + wave)) -
+                         cbase[r / TPC] + ex[r];
+            // side index: every 256th symbol starts on a lane with
+            // lane % 16 == 0 (a chunk has TPC * 32 sub-streams, so the
+            // unit's run from s * 256)
+            if ((lane & 15) == 0) {
+                uint32_t *so = sub_off + (uint64_t)s * (kUTiles * kUTile / kSub) + (tid >> 4);
+#pragma unroll
+                for (uint32_t r = 0; r < kUTiles; ++r) so[r * (kUTile / kSub)] = pos[r] - cw[r / TPC] * 32;
+            }
+            if (wave == 0 && lane == 0) publish_count(desc, s, words);
+        }
+        // ---- the previous unit: look-back, then its store ----------------
+        // (its count was published a round ago, so its predecessors have
+        // mostly published theirs)
+        if (have_a) {
+            if (wave == 0)
+                unit_meta(sh, desc, sa, words_a, lane, max_polls, status, chunk_bits, cwo, sa * NC, num_chunks, cbits_a,
+                          cw_a);
+            __syncthreads();
+            const uint64_t at = unit_excl(sh);
+            store_unit(sh.buf, payload + at, at, words_a, tid);
+        }
+        // the buffer is clear and every wave has read the totals
+        __syncthreads();
+        if (!live) break;
+        const uint32_t c0 = s * NC;
+        // the next unit's input is loaded while this one is placed (the
+        // last unit reads its own again: a conditional load would keep old
+        // values live)
+        const uint8_t *nsrc = in + (uint64_t)(s_next < num_units ? s_next : s) * (kUTiles * kUTile) + tid * 16;
+        if (words <= kUBufW - 2) {
+            // ---- phase 2: place every group, no barrier -----------------
+#pragma unroll
+            for (uint32_t r = 0; r < kUTiles; ++r) {
+                place_tile(tg[r], pos[r], sh.buf);
+                x[r] = load_stream16(nsrc + r * kUTile);
+                asm volatile("" ::: "memory");
+            }
+            have_a = true;
+            sa = s;
+            words_a = words;
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                cbits_a[k] = cbits[k];
+                cw_a[k] = cw[k];
+            }
+        } else {
+            // ---- a unit that does not fit the buffer (only data that does
+            // not compress): its look-back now, then two halves of four
+            // tiles (each fits) -------------------------------------------
+            if (wave == 0) unit_meta(sh, desc, s, words, lane, max_polls, status, chunk_bits, cwo, c0, num_chunks, cbits, cw);
+            constexpr uint32_t kHalf = kUTiles / 2;
+#pragma unroll
+            for (uint32_t r = 0; r < kHalf; ++r) place_tile(tg[r], pos[r], sh.buf);
+            __syncthreads();
+            const uint64_t excl = unit_excl(sh);
+            // unit word fb holds the bits of both halves; whole words
+            // before it go out, it moves to buf[0]
+            const uint32_t k = kHalf / TPC;
+            const uint32_t fb =
+                (cw[k] * 32 + (uint32_t)__builtin_amdgcn_readlane((int)exs, (int)(kHalf * kUW)) - cbase[k]) >> 5;
+            for (uint32_t i = tid; i < fb; i += kUT) payload[excl + i] = sh.buf[i];
+            const uint32_t carry = sh.buf[fb];
+            __syncthreads();
+            for (uint32_t i = tid; i <= fb + 2; i += kUT) sh.buf[i] = i == 0 ? carry : 0u;
+            __syncthreads();
+#pragma unroll
+            for (uint32_t r = kHalf; r < kUTiles; ++r) place_tile(tg[r], pos[r] - fb * 32, sh.buf);
+            __syncthreads();
+            store_unit(sh.buf, payload + excl + fb, excl + fb, words - fb, tid);
+#pragma unroll
+            for (uint32_t r = 0; r < kUTiles; ++r) x[r] = load_stream16(nsrc + r * kUTile);
+            __syncthreads();
+            have_a = false;
+        }
+        s = s_next;
+    }
+}
+
 // Any chunk size: the counting pass and the packing pass each read the
 // chunk (the second read is served by the caches for moderate chunks).
-// A workgroup's ticket t is its look-back index; it encodes chunk t + coff
-// (coff > 0 when a launch of multi-chunk workgroups went first).
+// A workgroup takes ticket t from counter `counter` (0 or 1) of workspace
+// word 0; its look-back index is t + dbase and it encodes chunk t + cbase
+// (a launch of multi-chunk workgroups may go first).
 __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint64_t n, uint32_t chunk,
     uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
-    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws, uint32_t coff,
-    uint32_t *__restrict__ status, uint32_t max_polls) {
+    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws, uint32_t counter,
+    uint32_t dbase, uint32_t cbase, uint32_t *__restrict__ status, uint32_t max_polls) {
     using SH = Shared<kThreads>;
     __shared__ SH sh;
     const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) sh.misc[0] = atomicAdd(reinterpret_cast<uint32_t *>(ws), 1u);
+    if (tid == 0) sh.misc[0] = atomicAdd(reinterpret_cast<uint32_t *>(ws) + counter, 1u) + dbase;
     {
         const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
         sh.code[tid] = reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid];
@@ -519,7 +782,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     for (uint32_t i = tid; i < SH::kStage; i += kThreads) sh.stage[i] = 0;
     __syncthreads();
     const uint32_t t = uniform(sh.misc[0]);
-    const uint32_t c = t + coff;
+    const uint32_t c = t - dbase + cbase;
     const uint64_t base = (uint64_t)c * chunk;
     const uint32_t lenc = (uint32_t)((n - base) < chunk ? (n - base) : chunk);
     const uint32_t ntiles = (lenc + kTile - 1) / kTile;
@@ -610,7 +873,8 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
     // one chunk per workgroup, so that a small input still spreads over the
     // CUs (the 1-chunk buffers hold 12 bits per symbol).
     constexpr uint64_t kManySmall = 8192;
-    uint64_t done = 0, tickets = 0;  // chunks and workgroups of the multi-chunk launch
+    uint64_t done = 0, tickets = 0;  // chunks and look-back indices of the multi-chunk launch
+    uint32_t counter = 0;            // the ticket counter of the re-reading kernel
 #define PC_ENC(T, NT, BW, TPC)                                                                             \
     do {                                                                                                   \
         const uint64_t nsup = nfull / ((NT) / (TPC));                                                      \
@@ -622,7 +886,34 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
             tickets = nsup;                                                                                \
         }                                                                                               \
     } while (0)
-    if (chunk == 65536) PC_ENC(1024, 4, 16392, 4);
+#define PC_ENC_UNIT(TPC)                                                                                   \
+    do {                                                                                                   \
+        const uint64_t nunits = nfull / (kUTiles / (TPC));                                                 \
+        uint64_t grid = 2 * (uint64_t)cus;                                                                 \
+        if (grid > nunits) grid = nunits;                                                                  \
+        hipLaunchKernelGGL((encode_unit_kernel<TPC>), dim3((uint32_t)grid), dim3(kUT), 0, stream, cb, in,  \
+                           (uint32_t)nc, (uint32_t)nunits, payload, chunk_bits, cwo, sub_off, ws, status,  \
+                           max_polls);                                                                     \
+        done = nunits * (kUTiles / (TPC));                                                                 \
+        tickets = nunits;                                                                                  \
+        counter = 1;                                                                                       \
+    } while (0)
+    // 64, 32 and 16 KiB chunks: the persistent unit kernel once every
+    // workgroup gets at least four units (it keeps two in flight; below
+    // that the chunk kernels, which start all their workgroups at once, are
+    // as fast or faster, measured)
+    int cus = 0;
+    if (chunk == 65536 || chunk == 32768 || chunk == 16384) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    const bool units = nfull * chunk >= (uint64_t)cus * 8 * kUTiles * kUTile && cus > 0;
+    if (chunk == 65536 && units) PC_ENC_UNIT(8);
+    else if (chunk == 32768 && units) PC_ENC_UNIT(4);
+    else if (chunk == 16384 && units) PC_ENC_UNIT(2);
+    else if (chunk == 65536) PC_ENC(1024, 4, 16392, 4);
     else if (chunk == 32768) PC_ENC(1024, 4, 16392, 2);
     else if (chunk == 16384) PC_ENC(1024, 4, 16392, 1);
     else if (chunk == 8192 && nfull >= kManySmall) PC_ENC(256, 8, 8200, 2);
@@ -630,13 +921,20 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
     else if (chunk == 4096 && nfull >= kManySmall) PC_ENC(256, 8, 8200, 1);
     else if (chunk == 4096) PC_ENC(256, 1, 1536, 1);
     const uint64_t rest = nc - done;
-    // tickets continue from the multi-chunk launch's: ticket t encodes
-    // chunk t + done - tickets
-    if (rest)
+    // look-back indices continue from the multi-chunk launch's: after the
+    // chunk kernels (which take exactly `tickets` tickets from counter 0)
+    // ticket t encodes chunk t + done - tickets; after the persistent unit
+    // kernel (which may take extra tickets of counter 0) the tickets of
+    // counter 1 start at 0, look-back index tickets + t, chunk done + t
+    if (rest) {
+        const uint32_t dbase = counter ? (uint32_t)tickets : 0u;
+        const uint32_t cbase = counter ? (uint32_t)done : (uint32_t)(done - tickets);
         hipLaunchKernelGGL(encode_kernel_any, dim3((uint32_t)rest), dim3(kThreads), 0, stream, cb, in, n, chunk,
-                           (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws, (uint32_t)(done - tickets), status,
+                           (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws, counter, dbase, cbase, status,
                            max_polls);
+    }
 #undef PC_ENC
+#undef PC_ENC_UNIT
     return hipGetLastError();
 }
 

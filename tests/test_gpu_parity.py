@@ -127,6 +127,38 @@ def test_stream_1g_full_size():
     assert int(host(enc)["chunk_bits"].astype(np.int64).sum()) == cb.coded_bits(xc, obook["lengths"])
 
 
+@pytest.mark.parametrize("chunk", [65536, 32768, 16384])
+def test_persistent_unit_path(chunk):
+    """Inputs large enough for the persistent 64 KiB-unit encoder (four
+    units per workgroup at two workgroups per CU), with whole chunks and a
+    short chunk left over for the re-reading kernel, and units of symbols
+    whose codes are 10 bits or longer (more than the buffer holds at once,
+    so they go out in two halves), compared in full with the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = 8 * cus * 65536 + 3 * chunk + 100
+    counts = random_counts(7)
+    dcb, obook = make_book(counts)
+    lengths = np.asarray(obook["lengths"])
+    long_syms = np.flatnonzero(lengths >= 10).astype(np.uint8)
+    assert long_syms.size > 0
+    say("unit path: chunk", chunk, "n", n, "long symbols", long_syms.size)
+    x_np = skewed(n, chunk)
+    rng = np.random.default_rng(chunk)
+    for u in (1, 37, 8 * cus - 1):  # whole 64 KiB units of long codes
+        x_np[u * 65536:(u + 1) * 65536] = rng.choice(long_syms, 65536)
+    x, enc = gpu_encode(dcb, x_np, chunk)
+    got = host(enc)
+    cwo = got["chunk_word_offset"].astype(np.int64)
+    per = 65536 // chunk
+    assert (cwo[38 * per] - cwo[37 * per]) > 16384  # that unit did not fit
+    want = coder.encode(x_np, obook["lengths"], obook["codes"], chunk, threads=16)
+    assert_same_stream(got, want)
+    out, status = pc.pc_decode(dcb, enc)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(out, x)
+
+
 def skewed(n, seed):
     rng = np.random.default_rng(seed)
     return ((rng.zipf(1.4, n) * 37) % 256).astype(np.uint8)
