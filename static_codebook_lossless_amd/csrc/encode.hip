@@ -635,10 +635,16 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
     bool have_a = false;
     uint32_t sa = 0, words_a = 0, cbits_a[NC], cw_a[NC];
     while (true) {
+        // the lane index passes an opaque step each round, so that values
+        // derived from it are recomputed rather than held (and spilled)
+        // across the loop
+        uint32_t tl = tid;
+        asm volatile("" : "+v"(tl));
+        const uint32_t ln = tl & 63;
         const bool live = s < num_units;
         // ---- phase 1: lookups, groups, wave scans ----------------------
         TileGroups tg[kUTiles];
-        uint32_t ex[kUTiles];  // bits before the lane within its wave, per tile
+        uint32_t ex[kUTiles];  // bits before the ln within its wave, per tile
         if (live) {
 #pragma unroll
             for (uint32_t r = 0; r < kUTiles; ++r) {
@@ -651,11 +657,11 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
                 lane_groups(x[r], sh, g, ng);
                 const uint32_t bits = ng[0] + ng[1] + ng[2] + ng[3];
                 const uint32_t incl = wave_incl_scan(bits);
-                if (lane == 63) sh.wtot[r * kUW + wave] = incl;
+                if (ln == 63) sh.wtot[r * kUW + wave] = incl;
                 ex[r] = incl - bits;
                 keep_groups(g, ng, tg[r]);
             }
-            if (tid == 0) sh.misc[1] = atomicAdd(ticket, 1u);
+            if (tl == 0) sh.misc[1] = atomicAdd(ticket, 1u);
         }
         __syncthreads();
         // ---- offsets: a scan over the 64 (tile, wave) totals -------------
@@ -663,7 +669,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         uint32_t cbase[NC], cbits[NC], cw[NC], pos[kUTiles];
         if (live) {
             s_next = uniform(sh.misc[1]);
-            const uint32_t v = sh.wtot[lane];
+            const uint32_t v = sh.wtot[ln];
             const uint32_t incl = wave_incl_scan(v);
             exs = incl - v;
             uint32_t cword = 0;
@@ -676,32 +682,32 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
                 cword += (cbits[k] + 31) >> 5;
             }
             words = cword;
-            // the lane's first bit of tile r in the unit's buffer (chunk k
+            // the ln's first bit of tile r in the unit's buffer (chunk k
             // of the unit starts on word cw[k])
 #pragma unroll
             for (uint32_t r = 0; r < kUTiles; ++r)
                 pos[r] = cw[r / TPC] * 32 + (uint32_t)__builtin_amdgcn_readlane((int)exs, (int)(r * kUW + wave)) -
                          cbase[r / TPC] + ex[r];
-            // side index: every 256th symbol starts on a lane with
-            // lane % 16 == 0 (a chunk has TPC * 32 sub-streams, so the
+            // side index: every 256th symbol starts on a ln with
+            // ln % 16 == 0 (a chunk has TPC * 32 sub-streams, so the
             // unit's run from s * 256)
-            if ((lane & 15) == 0) {
-                uint32_t *so = sub_off + (uint64_t)s * (kUTiles * kUTile / kSub) + (tid >> 4);
+            if ((ln & 15) == 0) {
+                uint32_t *so = sub_off + (uint64_t)s * (kUTiles * kUTile / kSub) + (tl >> 4);
 #pragma unroll
                 for (uint32_t r = 0; r < kUTiles; ++r) so[r * (kUTile / kSub)] = pos[r] - cw[r / TPC] * 32;
             }
-            if (wave == 0 && lane == 0) publish_count(desc, s, words);
+            if (wave == 0 && ln == 0) publish_count(desc, s, words);
         }
         // ---- the previous unit: look-back, then its store ----------------
         // (its count was published a round ago, so its predecessors have
         // mostly published theirs)
         if (have_a) {
             if (wave == 0)
-                unit_meta(sh, desc, sa, words_a, lane, max_polls, status, chunk_bits, cwo, sa * NC, num_chunks, cbits_a,
+                unit_meta(sh, desc, sa, words_a, ln, max_polls, status, chunk_bits, cwo, sa * NC, num_chunks, cbits_a,
                           cw_a);
             __syncthreads();
             const uint64_t at = unit_excl(sh);
-            store_unit(sh.buf, payload + at, at, words_a, tid);
+            store_unit(sh.buf, payload + at, at, words_a, tl);
         }
         // the buffer is clear and every wave has read the totals
         __syncthreads();
@@ -710,7 +716,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         // the next unit's input is loaded while this one is placed (the
         // last unit reads its own again: a conditional load would keep old
         // values live)
-        const uint8_t *nsrc = in + (uint64_t)(s_next < num_units ? s_next : s) * (kUTiles * kUTile) + tid * 16;
+        const uint8_t *nsrc = in + (uint64_t)(s_next < num_units ? s_next : s) * (kUTiles * kUTile) + tl * 16;
         if (words <= kUBufW - 2) {
             // ---- phase 2: place every group, no barrier -----------------
 #pragma unroll
@@ -731,7 +737,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
             // ---- a unit that does not fit the buffer (only data that does
             // not compress): its look-back now, then two halves of four
             // tiles (each fits) -------------------------------------------
-            if (wave == 0) unit_meta(sh, desc, s, words, lane, max_polls, status, chunk_bits, cwo, c0, num_chunks, cbits, cw);
+            if (wave == 0) unit_meta(sh, desc, s, words, ln, max_polls, status, chunk_bits, cwo, c0, num_chunks, cbits, cw);
             constexpr uint32_t kHalf = kUTiles / 2;
 #pragma unroll
             for (uint32_t r = 0; r < kHalf; ++r) place_tile(tg[r], pos[r], sh.buf);
@@ -742,15 +748,15 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
             const uint32_t k = kHalf / TPC;
             const uint32_t fb =
                 (cw[k] * 32 + (uint32_t)__builtin_amdgcn_readlane((int)exs, (int)(kHalf * kUW)) - cbase[k]) >> 5;
-            for (uint32_t i = tid; i < fb; i += kUT) payload[excl + i] = sh.buf[i];
+            for (uint32_t i = tl; i < fb; i += kUT) payload[excl + i] = sh.buf[i];
             const uint32_t carry = sh.buf[fb];
             __syncthreads();
-            for (uint32_t i = tid; i <= fb + 2; i += kUT) sh.buf[i] = i == 0 ? carry : 0u;
+            for (uint32_t i = tl; i <= fb + 2; i += kUT) sh.buf[i] = i == 0 ? carry : 0u;
             __syncthreads();
 #pragma unroll
             for (uint32_t r = kHalf; r < kUTiles; ++r) place_tile(tg[r], pos[r] - fb * 32, sh.buf);
             __syncthreads();
-            store_unit(sh.buf, payload + excl + fb, excl + fb, words - fb, tid);
+            store_unit(sh.buf, payload + excl + fb, excl + fb, words - fb, tl);
 #pragma unroll
             for (uint32_t r = 0; r < kUTiles; ++r) x[r] = load_stream16(nsrc + r * kUTile);
             __syncthreads();
