@@ -36,7 +36,7 @@ KERNEL_SOURCES = {
     "encode": os.path.join(ROOT, "static_codebook_lossless_amd", "csrc", "encode.hip"),
     "decode": os.path.join(ROOT, "static_codebook_lossless_amd", "csrc", "decode.hip"),
 }
-KERNEL_NAMES = {"encode": "encode_chunk_kernel", "decode": "decode_kernel<0>"}
+KERNEL_NAMES = {"encode": "encode_unit_kernel", "decode": "decode_kernel<0>"}
 
 
 def log(*a):
@@ -69,36 +69,44 @@ def _read_counter_csv(d, counter):
 
 
 def pmc_summary(fetch_dir, write_dir, copy_bytes, out=TRAFFIC_FILE):
-    """Per-dispatch HBM bytes of the coder kernels.  The plain device copy of
-    copy_bytes bytes that bench.py runs (it reads copy_bytes and writes
-    copy_bytes) calibrates each counter: scale = copy_bytes / counter(copy)."""
+    """Per-dispatch HBM bytes of the coder kernels.  bench.py copies
+    copy_bytes bytes twice: with the runtime's copy kernel, and with
+    pc_traffic_probe, which uses the coder kernels' own 16-byte non-temporal
+    loads and stores.  Each reads copy_bytes and writes copy_bytes, so
+    scale = copy_bytes / counter(copy).  The probe's scale converts the coder
+    kernels' counts; the runtime copy's is printed beside it as a check."""
     res = {}
+    copy_bytes16 = copy_bytes // 16 * 16
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = {}
         for name, val in _read_counter_csv(d, counter):
             per.setdefault(name, []).append(val * 1024.0)  # KiB -> bytes
-        copy_vals = [max(vs) for k, vs in per.items() if "copyBuffer" in k]
-        if not copy_vals:
-            raise RuntimeError("no copy kernel found for the %s scale" % counter)
-        scale = copy_bytes / max(copy_vals)
-        res[counter] = {"scale": scale, "kernels": {k: sorted(v)[len(v) // 2] for k, v in per.items()}}
+        blit = [max(vs) for k, vs in per.items() if "copyBuffer" in k]
+        probe = [sorted(vs)[len(vs) // 2] for k, vs in per.items() if "probe_copy_kernel" in k]
+        if not blit or not probe:
+            raise RuntimeError("no calibration copy found for the %s scale" % counter)
+        res[counter] = {"scale_blit": copy_bytes / max(blit), "scale": copy_bytes16 / probe[0],
+                        "kernels": {k: sorted(v)[len(v) // 2] for k, v in per.items()}}
+    labels = ["copyBuffer", "probe_copy_kernel"] + list(KERNEL_NAMES.values())
     lines = ["# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of bench.py.",
              "# Made by (from the repository root, after cd /tmp && export TMPDIR=/tmp):",
              "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o bench -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-secondary" % fetch_dir,
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs" % fetch_dir,
              "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o bench -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-secondary" % write_dir,
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs" % write_dir,
              "#   python3 bench.py --pmc-summary %s %s" % (fetch_dir, write_dir),
-             "# Each counter is scaled by copy_bytes / counter(plain device copy of copy_bytes bytes).",
+             "# Each counter is scaled by copy_bytes / counter(copy of copy_bytes bytes made with the coder",
+             "# kernels' 16-byte non-temporal loads and stores, pc_traffic_probe); the scale from the runtime's",
+             "# copy kernel (copyBuffer) is given beside it.",
              "# Raw medians (KiB per dispatch): " + "; ".join(
                  "%s %s %.1f" % (c, lab, v / 1024.0)
                  for c in ("FETCH_SIZE", "WRITE_SIZE")
                  for k, v in res[c]["kernels"].items()
-                 for lab in [next((kn for kn in ["copyBuffer"] + list(KERNEL_NAMES.values()) if kn in k), None)]
+                 for lab in [next((kn for kn in labels if kn in k), None)]
                  if lab),
              "copy_bytes %d" % copy_bytes,
-             "fetch_scale %.6f" % res["FETCH_SIZE"]["scale"],
-             "write_scale %.6f" % res["WRITE_SIZE"]["scale"]]
+             "fetch_scale %.6f (copyBuffer %.6f)" % (res["FETCH_SIZE"]["scale"], res["FETCH_SIZE"]["scale_blit"]),
+             "write_scale %.6f (copyBuffer %.6f)" % (res["WRITE_SIZE"]["scale"], res["WRITE_SIZE"]["scale_blit"])]
     for kind, kname in KERNEL_NAMES.items():
         f = [v for k, v in res["FETCH_SIZE"]["kernels"].items() if kname in k]
         w = [v for k, v in res["WRITE_SIZE"]["kernels"].items() if kname in k]
@@ -460,6 +468,17 @@ def main():
     ce1.record()
     torch.cuda.synchronize()
     copy_GBps = 2 * n * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
+    # the same copy through the coder kernels' own 16-byte non-temporal loads
+    # and stores (calibrates the hardware traffic counters, see pmc_summary)
+    n16 = n // 16 * 16
+    for _ in range(2):
+        pc.pc_traffic_probe(x[:n16], cpy[:n16])
+    ce0.record()
+    for _ in range(5):
+        pc.pc_traffic_probe(x[:n16], cpy[:n16])
+    ce1.record()
+    torch.cuda.synchronize()
+    probe_GBps = 2 * n16 * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
     del cpy
 
     def step(evs=None):
@@ -599,6 +618,7 @@ def main():
                            "frac": round(other_ach / HBM_PEAK_GBPS, 4),
                            "frac_of_device_copy": round(other_ach / copy_GBps, 4)},
         "device_copy_GBps": round(copy_GBps, 1),
+        "probe_copy_GBps": round(probe_GBps, 1),
         "bits_per_symbol": {"payload": round(b_payload, 5), "with_side_index": round(b_total, 5),
                             "entropy": round(H, 5), "per_shard_huffman12": round(shard_bits, 5),
                             "gap_vs_entropy_rel": round(b_payload / H - 1, 5),

@@ -289,6 +289,17 @@ pc_status pc_decode_qlc(const pc_codebook *d_cb, const uint32_t *d_payload, size
  */
 pc_status pc_histogram(const uint8_t *d_in, size_t n, uint64_t *d_counts, void *stream);
 
+/*
+ * Measurement helper, not part of the coding method: copies `bytes` bytes
+ * from d_src to d_dst with the 16-byte non-temporal loads and stores the
+ * coder kernels use, so that the HBM bytes hardware counters report for this
+ * known transfer (read `bytes`, write `bytes`) can calibrate the counts
+ * taken on the coder kernels.  Both pointers 16-byte aligned device memory,
+ * bytes a multiple of 16 (PC_ERR_INVALID_ARG otherwise); asynchronous on
+ * `stream`; bytes == 0 does nothing.
+ */
+pc_status pc_traffic_probe(const void *d_src, void *d_dst, size_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

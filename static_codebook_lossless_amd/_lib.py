@@ -27,6 +27,7 @@ EXPORTS = [
     "pc_shard_code_lengths",
     "pc_num_chunks", "pc_num_substreams", "pc_max_payload_words", "pc_encode_workspace_bytes",
     "pc_encode", "pc_encode_noalloc", "pc_encode_set_wait_limit", "pc_decode", "pc_decode_qlc", "pc_histogram",
+    "pc_traffic_probe",
 ]
 
 
@@ -59,9 +60,10 @@ def _load():
     lib.pc_decode.argtypes = [p, p, sz, p, p, p, sz, sz, p, p, p]
     lib.pc_decode_qlc.argtypes = [p, p, sz, p, p, p, sz, sz, p, p, p]
     lib.pc_histogram.argtypes = [p, sz, p, p]
+    lib.pc_traffic_probe.argtypes = [p, p, sz, p]
     for f in ("pc_codebook_build", "pc_codebook_validate", "pc_qlc_optimal_bits", "pc_codebook_fit",
               "pc_shard_code_lengths", "pc_encode", "pc_encode_noalloc",
-              "pc_decode", "pc_decode_qlc", "pc_histogram"):
+              "pc_decode", "pc_decode_qlc", "pc_histogram", "pc_traffic_probe"):
         getattr(lib, f).restype = i
     return lib
 
@@ -278,3 +280,13 @@ def pc_histogram(d_in: torch.Tensor, counts: torch.Tensor | None = None) -> torc
         counts = torch.zeros(256, dtype=torch.int64, device=x.device)
     _check(lib.pc_histogram(_ptr(x), x.numel(), _ptr(counts), _stream(x.device)), "pc_histogram")
     return counts
+
+
+def pc_traffic_probe(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Copy ``src`` into ``dst`` (same byte size, a multiple of 16) with the
+    coder kernels' 16-byte non-temporal loads and stores: a known transfer
+    for calibrating hardware traffic counters."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not (src.is_cuda and dst.is_cuda):
+        raise ValueError("pc_traffic_probe: src and dst must be device tensors of the same byte size")
+    _check(lib.pc_traffic_probe(_ptr(src), _ptr(dst), nbytes, _stream(src.device)), "pc_traffic_probe")

@@ -9,8 +9,8 @@
 // workgroup); its payload is one contiguous span of words.  Workgroups are
 // persistent and walk the groups with a stride of the grid size.  While a
 // workgroup decodes group k out of LDS, the loads of group k+1 (its
-// container entries, then its payload span into registers, two 16-byte
-// loads per lane after each of the steps 0-7 of the first 128 symbols; the
+// container entries, then its payload span into registers, one 16-byte
+// load per lane after each of the 16 steps of the first 128 symbols; the
 // span's entries come one group earlier still) are in flight, so HBM
 // latency is hidden behind decoding.  Per group:
 //   1. the staged span sits in LDS as contiguous words (a span starts on a
@@ -297,6 +297,7 @@ __device__ __forceinline__ uint32_t vgpr_copy(uint32_t v) {
 // is decoded, see store_group).
 constexpr uint32_t kHalf = kSub / 2;
 constexpr uint32_t kHalfWords = kHalf / 4;
+static_assert(kPrefetch == kHalf / 8, "one prefetch load per step of a half");
 
 // side(q) runs after step q (8 symbols) of the 16: the memory instructions
 // of a group are spread over its decode steps, where the wave mostly waits
@@ -646,13 +647,13 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
         const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
         const LdsWords src{stage, (uint32_t)((cnt < stage_cap ? cnt : stage_cap) - (cnt > 0 ? 1 : 0))};
         uint32_t bad = no_invalid_yet<MODE>();
-        // first half: the next group's payload loads, two per step from step
-        // 0 (its span entries were loaded one group ahead)
+        // first half: the next group's payload loads, one per step (spread
+        // thinner than two per step over half the steps: measured faster);
+        // its span entries were loaded one group ahead
         uint32_t pos = decode_half<MODE, CHECK>(src, job.pos0, t, bad, o1, [&](uint32_t q) {
-            if (2 * q < kPrefetch) prefetch_quad(pf, 2 * q, pq, nq_lo, nq_last, tid);
-            if (2 * q + 1 < kPrefetch) prefetch_quad(pf, 2 * q + 1, pq, nq_lo, nq_last, tid);
+            prefetch_quad(pf, q, pq, nq_lo, nq_last, tid);
         });
-        pos = decode_half<MODE, CHECK>(src, pos, t, bad, o2, [&](uint32_t q) {});
+        pos = decode_half<MODE, CHECK>(src, pos, t, bad, o2, [&](uint32_t) {});
         if (staged && job.ok && (saw_invalid<MODE>(bad, t) || pos != job.pos_want)) flag_corrupt(status);
         // the staging rows take the output once every lane is done with them
         __syncthreads();

@@ -87,3 +87,11 @@ def test_size_limits():
     for fn in (lib.pc_decode, lib.pc_decode_qlc):
         assert dec(fn, n=(0xFFFFFF00) * 256, chunk=1 << 24) == pc.PC_ERR_UNSUPPORTED
         assert dec(fn, n=big) == pc.PC_ERR_UNSUPPORTED
+
+
+def test_traffic_probe_args():
+    assert lib.pc_traffic_probe(None, None, 0, None) == pc.PC_OK
+    assert lib.pc_traffic_probe(None, A, 64, None) == pc.PC_ERR_INVALID_ARG
+    assert lib.pc_traffic_probe(A, None, 64, None) == pc.PC_ERR_INVALID_ARG
+    assert lib.pc_traffic_probe(A, A, 63, None) == pc.PC_ERR_INVALID_ARG
+    assert lib.pc_traffic_probe(ODD, A, 64, None) == pc.PC_ERR_INVALID_ARG

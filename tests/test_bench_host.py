@@ -48,3 +48,39 @@ def test_oracle_parity_leg_on_oracle_streams():
     host["payload"][3] ^= 1
     got = bench.oracle_parity((x, counts, "huffman", None, 4096, host), 2)
     assert not got["payload"] and got["chunk_bits"] and got["oracle_round_trip"]
+
+
+def test_pmc_summary_scales_by_the_probe_copy(tmp_path):
+    """Counter summary on hand-made rocprofv3 CSVs: both calibration copies
+    move copy_bytes each way; the probe's scale converts the coder kernels'
+    counts, the runtime copy's is printed beside it."""
+    import csv
+
+    cb_ = 1 << 20
+    rows = {  # KiB per dispatch
+        "FETCH_SIZE": [("__amd_rocclr_copyBuffer", 512.0), ("pc::probe_copy_kernel(...)", 512.0),
+                       ("pc::encode_unit_kernel<8>(...)", 600.0), ("pc::decode_kernel<0>(...)", 400.0),
+                       ("pc::decode_kernel<0>(...)", 420.0), ("pc::decode_kernel<0>(...)", 410.0)],
+        "WRITE_SIZE": [("__amd_rocclr_copyBuffer", 1024.0), ("pc::probe_copy_kernel(...)", 1000.0),
+                       ("pc::encode_unit_kernel<8>(...)", 800.0), ("pc::decode_kernel<0>(...)", 1024.0)],
+    }
+    dirs = {}
+    for counter, rs in rows.items():
+        d = tmp_path / counter
+        d.mkdir()
+        with open(d / "bench_counter_collection.csv", "w", newline="") as f:
+            wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+            wr.writeheader()
+            for k, v in rs:
+                wr.writerow({"Kernel_Name": k, "Counter_Name": counter, "Counter_Value": v})
+        dirs[counter] = str(d)
+    out = tmp_path / "traffic.txt"
+    bench.pmc_summary(dirs["FETCH_SIZE"], dirs["WRITE_SIZE"], cb_, out=str(out))
+    text = out.read_text()
+    assert "fetch_scale 2.000000 (copyBuffer 2.000000)" in text
+    assert "write_scale 1.024000 (copyBuffer 1.000000)" in text
+    kern = {l.split()[1]: l.split() for l in text.splitlines() if l.startswith("kernel ")}
+    # (printed to whole bytes)
+    assert abs(float(kern["encode"][5]) - 600.0 * 1024 * 2) < 1
+    assert abs(float(kern["encode"][7]) - 800.0 * 1024 * 1.024) < 1
+    assert abs(float(kern["decode"][5]) - 410.0 * 1024 * 2) < 1  # the median dispatch

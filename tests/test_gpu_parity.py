@@ -561,3 +561,15 @@ def test_encode_wait_give_up_is_reported():
     assert int(enc.status.item()) == pc.PC_OK
     want = coder.encode(x_np, obook["lengths"], obook["codes"], w.chunk, threads=8)
     assert_same_stream(host(enc), want)
+
+
+def test_traffic_probe_copies():
+    """The counter-calibration copy moves the bytes unchanged (sizes around
+    one grid pass and a ragged tail of 16-byte quads)."""
+    rng = np.random.default_rng(5)
+    for nbytes in (16, 4096 + 48, (1 << 22) + 16 * 7):
+        src = torch.from_numpy(rng.integers(0, 256, nbytes, dtype=np.uint8)).to(DEV)
+        dst = torch.zeros_like(src)
+        pc.pc_traffic_probe(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst)
