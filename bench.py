@@ -120,6 +120,88 @@ def pmc_summary(fetch_dir, write_dir, copy_bytes, out=TRAFFIC_FILE):
     print("\n".join(lines))
 
 
+def _short_kernel(name):
+    n = name.replace("pc::(anonymous namespace)::", "").replace("pc::", "")
+    i = n.find("(")
+    return n[:i] if i > 0 else n
+
+
+def trace_summary(trace_dir, out, command):
+    """Per-kernel lines (calls, average/min/max ns, share) from a
+    rocprofv3 --kernel-trace --stats --output-format csv run."""
+    import csv
+
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError("no kernel_stats.csv under " + trace_dir)
+    rows = []
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"]),
+                         float(r["Percentage"]), _short_kernel(r["Name"])))
+    rows.sort(key=lambda t: -t[4])
+    lines = ["# rocprofv3 kernel trace of bench.py on the 1 GiB e4m3 stream (64 KiB chunks, Huffman-12)",
+             "# Command (from the repository root, after cd /tmp && export TMPDIR=/tmp):",
+             "#   " + command,
+             "#   python3 bench.py --trace-summary %s" % trace_dir,
+             "# Columns: calls, average ns, min ns, max ns, share of GPU time, kernel"]
+    for c, avg, mn, mx, pct, name in rows[:12]:
+        lines.append("%6d %10.0f %10.0f %10.0f %7.2f%%  %s" % (c, avg, mn, mx, pct, name[:90]))
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# SQ counters summed over the device per dispatch; *_CYCLES and LEVEL
+# counters count in the SQ's own units (the ratios below only divide
+# counters of the same kind).
+SQ_RATIOS = [
+    ("VALU instructions per wave", "SQ_INSTS_VALU", "SQ_WAVES"),
+    ("LDS instructions per wave", "SQ_INSTS_LDS", "SQ_WAVES"),
+    ("VMEM instructions per wave", "SQ_INSTS_VMEM", "SQ_WAVES"),
+    ("SALU instructions per wave", "SQ_INSTS_SALU", "SQ_WAVES"),
+    ("VALU-active share of wave cycles", "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES"),
+    ("LDS-active share of wave cycles", "SQ_ACTIVE_INST_LDS", "SQ_WAVE_CYCLES"),
+    ("waiting-on-LDS share of wave cycles", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+    ("waiting-on-anything share of wave cycles", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+    ("LDS bank-conflict cycles per LDS-active cycle", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"),
+]
+
+
+def sq_summary(dirs, out, commands):
+    """Median per-dispatch SQ counters of the coder kernels, from one or more
+    rocprofv3 --pmc runs, and the ratios in SQ_RATIOS."""
+    vals = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise FileNotFoundError("no counter_collection.csv under " + d)
+        import csv
+
+        with open(files[0]) as f:
+            for r in csv.DictReader(f):
+                for kind, kname in KERNEL_NAMES.items():
+                    if kname in r["Kernel_Name"]:
+                        vals.setdefault(kind, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    med = {k: {c: sorted(v)[len(v) // 2] for c, v in cs.items()} for k, cs in vals.items()}
+    lines = ["# SQ counters of the coder kernels on the 1 GiB e4m3 stream (64 KiB chunks, Huffman-12),",
+             "# median over dispatches, summed over the device.",
+             "# Commands (from the repository root, after cd /tmp && export TMPDIR=/tmp):"]
+    lines += ["#   " + c for c in commands]
+    lines.append("#   python3 bench.py --sq-summary " + " ".join(dirs))
+    kinds = [k for k in KERNEL_NAMES if k in med]
+    counters = sorted({c for k in kinds for c in med[k]})
+    lines.append("%-44s " % "counter" + " ".join("%18s" % k for k in kinds))
+    for c in counters:
+        lines.append("%-44s " % c + " ".join("%18.0f" % med[k].get(c, float("nan")) for k in kinds))
+    for label, a, b in SQ_RATIOS:
+        if all(a in med[k] and b in med[k] and med[k][b] for k in kinds):
+            lines.append("%-44s " % label + " ".join("%18.4f" % (med[k][a] / med[k][b]) for k in kinds))
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def load_traffic(kind):
     """Scaled HBM bytes per dispatch of `kind`, or None when absent/stale."""
     if not os.path.exists(TRAFFIC_FILE):
@@ -400,6 +482,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR")
+    ap.add_argument("--trace-command", default="")
+    ap.add_argument("--sq-summary", nargs="+", metavar="PMC_DIR")
+    ap.add_argument("--sq-commands", nargs="*", default=[])
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the QLC (GELU tensor) and histogram measurements")
     ap.add_argument("--no-configs", action="store_true",
@@ -408,6 +494,14 @@ def main():
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.trace_summary:
+        trace_summary(args.trace_summary, os.path.join(ROOT, "profiles", "coder_kernels_stream_1g_kernel_trace.txt"),
+                      args.trace_command)
+        return 0
+    if args.sq_summary:
+        sq_summary(args.sq_summary, os.path.join(ROOT, "profiles", "coder_kernels_stream_1g_sq_counters.txt"),
+                   args.sq_commands)
+        return 0
     if args.pmc_summary:
         import workloads as W
 

@@ -101,7 +101,7 @@ typedef struct pc_codebook {
     uint8_t pad[8];
 } pc_codebook;
 
-/* Human-readable name of a status code (static storage). */
+/* Human-readable name of a status code (static storage; library-defined). */
 const char *pc_status_string(int status);
 
 /*
@@ -125,7 +125,12 @@ const char *pc_status_string(int status);
 pc_status pc_codebook_build(const uint64_t counts[256], int kind, const uint8_t qlc_bits[8],
                             pc_codebook *out);
 
-/* Host check of a codebook blob (magic, version, lengths, tables). */
+/*
+ * Host check of a codebook blob (magic, version, lengths, tables).  The
+ * pages define no codebook format (the single-stage page, abstract, only
+ * requires that encoder and decoder hold the same precomputed codebook);
+ * this checks the library's own layout above.
+ */
 pc_status pc_codebook_validate(const pc_codebook *cb);
 
 /*
@@ -173,7 +178,11 @@ pc_status pc_codebook_fit(const pc_codebook *cb, const uint64_t counts[256], dou
  */
 pc_status pc_shard_code_lengths(const uint64_t counts[256], uint8_t lengths_out[256]);
 
-/* Size queries (host, pure).  chunk must be a valid chunk size, else 0. */
+/*
+ * Size queries (host, pure) of the container above, which is the library's
+ * own (the pages define no container).  chunk must be a valid chunk size,
+ * else 0.  The payload bound uses the 12-bit length limit (PC_MAX_LEN).
+ */
 size_t pc_num_chunks(size_t n, size_t chunk);          /* ceil(n / chunk) */
 size_t pc_num_substreams(size_t n, size_t chunk);      /* sum over chunks of ceil(len_c / 256) */
 size_t pc_max_payload_words(size_t n, size_t chunk);   /* sum over chunks of ceil(12 len_c / 32) */
@@ -248,7 +257,11 @@ uint32_t pc_encode_set_wait_limit(uint32_t polls);
  * Decode n symbols (device, asynchronous on `stream`) with the generic
  * engine: one lane per 256-symbol sub-stream, one 12-bit peek per codeword
  * through the dec_sym/dec_len tables held in LDS.  Works for both codebook
- * kinds.
+ * kinds.  The decoder holds the same fixed codebook as the encoder, so no
+ * table travels with the data ("Single-Stage Huffman Encoder for ML
+ * Compression", abstract); one table lookup per codeword instead of a
+ * bit-by-bit tree walk is the decoding-speed concern of "Quad Length Codes
+ * for Lossless Compression of e4m3" (abstract).
  *   d_payload, payload_words   the payload (16-byte aligned) and its length;
  *              no word at or past payload_words is ever read.
  *   d_chunk_bits, d_chunk_word_offset, d_sub_off   as written by pc_encode.
@@ -286,6 +299,9 @@ pc_status pc_decode_qlc(const pc_codebook *d_cb, const uint32_t *d_payload, size
  * Byte histogram on the device: d_counts[s] += number of bytes equal to s in
  * d_in[0, n).  Accumulates, so pooling previous batches is repeated calls on
  * the same d_counts (256 u64, 8-byte aligned).  d_in needs no alignment.
+ * The pooled histogram of previous batches is what the fixed codebook is
+ * built from ("Single-Stage Huffman Encoder for ML Compression", abstract:
+ * the average distribution of previous data batches).
  */
 pc_status pc_histogram(const uint8_t *d_in, size_t n, uint64_t *d_counts, void *stream);
 

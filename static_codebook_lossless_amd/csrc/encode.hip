@@ -258,10 +258,8 @@ __device__ __forceinline__ void make_group(uint32_t e0, uint32_t e1, uint32_t e2
 
 // OR one group (ng bits of g) into the buffer at bit p (bit 0 = MSB of
 // buf[0]); it spans at most 3 words.  All three ORs are issued for every
-// lane (an OR with zero changes nothing): with the second and third made
-// conditional, exec-masked LDS atomics of this shape were seen to lose
-// updates on gfx950 (one wave's words of a tile came out with bits missing,
-// varying from run to run).
+// lane (an OR with zero changes nothing), which keeps the placement free of
+// branches.
 __device__ __forceinline__ void place_group(uint64_t g, uint32_t ng, uint32_t p, uint32_t *buf) {
     const uint64_t a = g << (64 - ng);
     const uint32_t hi = (uint32_t)(a >> 32), lo = (uint32_t)a;
@@ -713,16 +711,19 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         __syncthreads();
         if (!live) break;
         const uint32_t c0 = s * NC;
-        // the next unit's input is loaded while this one is placed (the
-        // last unit reads its own again: a conditional load would keep old
-        // values live)
-        const uint8_t *nsrc = in + (uint64_t)(s_next < num_units ? s_next : s) * (kUTiles * kUTile) + tl * 16;
+        // the next unit's input is loaded while this one is placed; after
+        // the last unit every lane reads the input's first 16 bytes (a
+        // load on every path: a conditional one would keep the old values
+        // live through both phases)
+        const bool more = s_next < num_units;
+        const uint8_t *nsrc = more ? in + (uint64_t)s_next * (kUTiles * kUTile) + tl * 16 : in;
+        const uint32_t nstride = more ? kUTile : 0u;
         if (words <= kUBufW - 2) {
             // ---- phase 2: place every group, no barrier -----------------
 #pragma unroll
             for (uint32_t r = 0; r < kUTiles; ++r) {
                 place_tile(tg[r], pos[r], sh.buf);
-                x[r] = load_stream16(nsrc + r * kUTile);
+                x[r] = load_stream16(nsrc + r * nstride);
                 asm volatile("" ::: "memory");
             }
             have_a = true;
@@ -758,7 +759,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
             __syncthreads();
             store_unit(sh.buf, payload + excl + fb, excl + fb, words - fb, tl);
 #pragma unroll
-            for (uint32_t r = 0; r < kUTiles; ++r) x[r] = load_stream16(nsrc + r * kUTile);
+            for (uint32_t r = 0; r < kUTiles; ++r) x[r] = load_stream16(nsrc + r * nstride);
             __syncthreads();
             have_a = false;
         }

@@ -573,3 +573,27 @@ def test_traffic_probe_copies():
         pc.pc_traffic_probe(src, dst)
         torch.cuda.synchronize()
         assert torch.equal(src, dst)
+
+
+def test_refresh_pools_on_the_device():
+    """CodebookRefresh.observe_batch (histograms counted and pooled by
+    pc_histogram on the device) makes the same rebuild decisions and the
+    same codebooks as observe on host histograms of the same batches,
+    including batches leaving the window, and its pool equals the sum of the
+    window's bincounts."""
+    rng = np.random.default_rng(17)
+    batches = []
+    for k in range(9):
+        scale = 1.0 if k < 5 else 4.0  # drift from batch 5 on
+        v = rng.standard_normal(1 << 16) * scale
+        batches.append(((np.clip(v, -7.9, 7.9) * 16).astype(np.int64) % 256).astype(np.uint8))
+    host = pc.CodebookRefresh(window=3, threshold=0.02)
+    dev = pc.CodebookRefresh(window=3, threshold=0.02)
+    for k, b in enumerate(batches):
+        a = host.observe(np.bincount(b, minlength=256))
+        d = dev.observe_batch(torch.from_numpy(b).to(DEV))
+        assert a == d, k
+        assert torch.equal(host.codebook, dev.codebook), k
+        want = sum(np.bincount(x, minlength=256) for x in batches[max(0, k - 2):k + 1])
+        assert np.array_equal(dev.pool_dev.cpu().numpy(), want), k
+    assert host.rebuilds == dev.rebuilds >= 2
