@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import shlex
 import json
 import math
 import os
@@ -126,7 +127,7 @@ def _short_kernel(name):
     return n[:i] if i > 0 else n
 
 
-def trace_summary(trace_dir, out, command):
+def trace_summary(trace_dir, out, command, title=None):
     """Per-kernel lines (calls, average/min/max ns, share) from a
     rocprofv3 --kernel-trace --stats --output-format csv run."""
     import csv
@@ -140,10 +141,10 @@ def trace_summary(trace_dir, out, command):
             rows.append((int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"]),
                          float(r["Percentage"]), _short_kernel(r["Name"])))
     rows.sort(key=lambda t: -t[4])
-    lines = ["# rocprofv3 kernel trace of bench.py on the 1 GiB e4m3 stream (64 KiB chunks, Huffman-12)",
+    lines = ["# " + (title or "rocprofv3 kernel trace of bench.py on the 1 GiB e4m3 stream (64 KiB chunks, Huffman-12)"),
              "# Command (from the repository root, after cd /tmp && export TMPDIR=/tmp):",
              "#   " + command,
-             "#   python3 bench.py --trace-summary %s" % trace_dir,
+             "#   python3 bench.py " + " ".join(shlex.quote(a) for a in sys.argv[1:]),
              "# Columns: calls, average ns, min ns, max ns, share of GPU time, kernel"]
     for c, avg, mn, mx, pct, name in rows[:12]:
         lines.append("%6d %10.0f %10.0f %10.0f %7.2f%%  %s" % (c, avg, mn, mx, pct, name[:90]))
@@ -484,6 +485,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--trace-summary", metavar="TRACE_DIR")
     ap.add_argument("--trace-command", default="")
+    ap.add_argument("--trace-out", default="coder_kernels_stream_1g_kernel_trace.txt")
+    ap.add_argument("--trace-title", default=None)
     ap.add_argument("--sq-summary", nargs="+", metavar="PMC_DIR")
     ap.add_argument("--sq-commands", nargs="*", default=[])
     ap.add_argument("--no-secondary", action="store_true",
@@ -495,8 +498,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.trace_summary:
-        trace_summary(args.trace_summary, os.path.join(ROOT, "profiles", "coder_kernels_stream_1g_kernel_trace.txt"),
-                      args.trace_command)
+        trace_summary(args.trace_summary, os.path.join(ROOT, "profiles", os.path.basename(args.trace_out)),
+                      args.trace_command, args.trace_title)
         return 0
     if args.sq_summary:
         sq_summary(args.sq_summary, os.path.join(ROOT, "profiles", "coder_kernels_stream_1g_sq_counters.txt"),

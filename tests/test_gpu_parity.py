@@ -563,6 +563,35 @@ def test_encode_wait_give_up_is_reported():
     assert_same_stream(host(enc), want)
 
 
+def test_unit_encoder_wait_limit_one_poll():
+    """The persistent unit encoder (an input of four units per workgroup)
+    with its bounded wait cut to one poll: every call ends, the status is
+    PC_OK or PC_ERR_TIMEOUT (a walk that met an unpublished predecessor gave
+    up), and with the default limit the same call is bit-exact again."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = 8 * cus * 65536
+    dcb, obook = make_book(random_counts(3))
+    x_np = skewed(n, 3)
+    x = torch.from_numpy(x_np).to(DEV)
+    outs = pc.alloc_encode_outputs(n, 65536, torch.device(DEV))
+    seen = []
+    prev = pc.pc_encode_set_wait_limit(1)
+    try:
+        for rep in range(3):
+            enc = pc.pc_encode(dcb, x, 65536, outputs=outs)
+            torch.cuda.synchronize()
+            seen.append(int(enc.status.item()))
+    finally:
+        pc.pc_encode_set_wait_limit(prev)
+    say("unit encoder, one-poll limit: statuses", seen)
+    assert set(seen) <= {pc.PC_OK, pc.PC_ERR_TIMEOUT}
+    enc = pc.pc_encode(dcb, x, 65536, outputs=outs)
+    torch.cuda.synchronize()
+    assert int(enc.status.item()) == pc.PC_OK
+    want = coder.encode(x_np, obook["lengths"], obook["codes"], 65536, threads=16)
+    assert_same_stream(host(enc), want)
+
+
 def test_traffic_probe_copies():
     """The counter-calibration copy moves the bytes unchanged (sizes around
     one grid pass and a ragged tail of 16-byte quads)."""
