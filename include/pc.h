@@ -186,7 +186,8 @@ pc_status pc_shard_code_lengths(const uint64_t counts[256], uint8_t lengths_out[
 size_t pc_num_chunks(size_t n, size_t chunk);          /* ceil(n / chunk) */
 size_t pc_num_substreams(size_t n, size_t chunk);      /* sum over chunks of ceil(len_c / 256) */
 size_t pc_max_payload_words(size_t n, size_t chunk);   /* sum over chunks of ceil(12 len_c / 32) */
-size_t pc_encode_workspace_bytes(size_t n, size_t chunk);
+size_t pc_encode_workspace_bytes(size_t n, size_t chunk);  /* 8 (1 + chunks), + 4 per 64 KiB of full
+                                                          chunks for chunks of several 64 KiB (rounded up to 8) */
 
 /*
  * Encode n symbols (device, asynchronous on `stream`): every byte becomes
@@ -228,7 +229,9 @@ pc_status pc_encode(const pc_codebook *d_cb, const uint8_t *d_in, size_t n, size
  * workspace: the cross-chunk scan's ticket and descriptors live in a static
  * device array of the library (8 MiB + 8 bytes per GPU, held until the
  * process ends), so the call allocates nothing.  At most 2^20 chunks per
- * call (PC_ERR_CAPACITY beyond).  Every call on one GPU shares that GPU's
+ * call, and pc_encode_workspace_bytes(n, chunk) at most that array's size
+ * (PC_ERR_CAPACITY beyond; it binds for chunks of several 64 KiB, which
+ * keep one u32 per 64 KiB in the array).  Every call on one GPU shares that GPU's
  * array and clears it first on its stream: calls that overlap on one GPU
  * (several streams, or host threads) race and must be serialised by the
  * caller, e.g. by issuing them on one stream.

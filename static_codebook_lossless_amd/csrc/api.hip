@@ -7,7 +7,8 @@
 
 // Workspace of pc_encode_noalloc: the ticket word and one look-back
 // descriptor per workgroup unit (at most one per chunk), for up to
-// kNoAllocMaxChunks chunks: 8 MiB + 8 bytes on every GPU the library runs
+// kNoAllocMaxChunks chunks (fewer for chunks of several 64 KiB units, whose
+// per-unit counts share the array): 8 MiB + 8 bytes on every GPU the library runs
 // on, held until the process ends.  Host code never uses the array's name
 // as an address: each device's copy is reached through the pointer
 // hipGetSymbolAddress returns for it (noalloc_scratch below).
@@ -87,7 +88,10 @@ extern "C" {
 
 size_t pc_encode_workspace_bytes(size_t n, size_t chunk) {
     if (!chunk_ok(chunk)) return 0;
-    return (1 + pc_num_chunks(n, chunk)) * sizeof(uint64_t);
+    // the ticket word and one look-back descriptor per chunk; chunks of
+    // several 64 KiB units also keep a u32 per unit of their full chunks
+    const size_t units = chunk > 65536 && chunk % 65536 == 0 ? (n / chunk) * (chunk / 65536) : 0;
+    return (1 + pc_num_chunks(n, chunk)) * sizeof(uint64_t) + (units + 1) / 2 * sizeof(uint64_t);
 }
 
 uint32_t pc_encode_set_wait_limit(uint32_t polls) {
@@ -113,7 +117,8 @@ pc_status pc_encode_noalloc(const pc_codebook *d_cb, const uint8_t *d_in, size_t
     pc_status st = check_encode_args(d_cb, d_in, n, chunk, d_payload, payload_capacity_words, d_chunk_bits,
                                      d_chunk_word_offset, d_sub_off, d_status);
     if (st != PC_OK) return st;
-    if (pc_num_chunks(n, chunk) > kNoAllocMaxChunks) return PC_ERR_CAPACITY;
+    if (pc_num_chunks(n, chunk) > kNoAllocMaxChunks || pc_encode_workspace_bytes(n, chunk) > sizeof(scratch))
+        return PC_ERR_CAPACITY;
     uint64_t *ws = nullptr;
     const hipError_t e = noalloc_scratch(&ws);
     if (e != hipSuccess) return PC_ERR_HIP;

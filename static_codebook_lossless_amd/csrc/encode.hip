@@ -611,7 +611,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
     uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws, uint32_t *__restrict__ status, uint32_t max_polls) {
     constexpr int NC = kUTiles / TPC;  // chunks per unit
     __shared__ UnitShared sh;
-    const uint32_t tid = threadIdx.x, lane = tid & 63;
+    const uint32_t tid = threadIdx.x;
     const uint32_t wave = uniform(tid >> 6);
     uint32_t *ticket = reinterpret_cast<uint32_t *>(ws);
     uint64_t *desc = ws + 1;
@@ -767,6 +767,195 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
     }
 }
 
+// ---------------------------------------------------------------------------
+// Chunks of a multiple of 64 KiB above 64 KiB.  A chunk is then several
+// 64 KiB units whose bitstreams join mid-word, so a unit cannot start on a
+// word boundary, and a look-back over units would have to round up to a
+// word at every chunk end.  Three launches instead, with no device-side
+// wait: count (every unit's bit count), scan (one workgroup: the chunks' bit
+// counts and word offsets, each unit's bit offset in its chunk, and the
+// payload words at unit edges cleared), place (every unit at its known
+// offset: inner words stored, the first and last word OR-ed in with device
+// atomics, since the neighbouring unit of the chunk may share them).  The
+// input is read twice.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kBigUnit = kUTiles * kUTile;  // 65536 symbols
+
+__global__ __launch_bounds__(256) void encode_count_kernel(const pc_codebook *__restrict__ cb,
+                                                           const uint8_t *__restrict__ in,
+                                                           uint32_t *__restrict__ unit_bits) {
+    __shared__ uint32_t len[256];
+    __shared__ uint32_t wsum[4];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    len[tid] = reinterpret_cast<const uint8_t *>(cb)[kOffLength + tid];
+    const uint8_t *src = in + (uint64_t)blockIdx.x * kBigUnit + tid * 16;
+    uint4 x[16];
+#pragma unroll
+    for (uint32_t r = 0; r < 16; ++r) x[r] = load_stream16(src + r * 4096);
+    __syncthreads();
+    uint32_t bits = 0;
+#pragma unroll
+    for (uint32_t r = 0; r < 16; ++r) {
+        const uint32_t w[4] = {x[r].x, x[r].y, x[r].z, x[r].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            bits += len[w[q] & 0xFF] + len[(w[q] >> 8) & 0xFF] + len[(w[q] >> 16) & 0xFF] + len[w[q] >> 24];
+    }
+    const uint32_t incl = wave_incl_scan(bits);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    if (tid == 0) unit_bits[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+// One workgroup.  In: unit_bits[u] for the nfull * U units.  Out:
+// chunk_bits and chunk_word_offset of the full chunks (cwo[nfull] = their
+// total words), unit_bits[u] replaced by the unit's bit offset in its chunk,
+// the payload words at both edges of every unit cleared, and descriptor 0
+// published inclusive with the total (a short last chunk looks back to it).
+__global__ __launch_bounds__(1024) void encode_unit_scan_kernel(uint32_t *__restrict__ unit_bits, uint32_t U,
+                                                                uint32_t nfull, uint32_t *__restrict__ chunk_bits,
+                                                                uint64_t *__restrict__ cwo,
+                                                                uint32_t *__restrict__ payload,
+                                                                uint64_t *__restrict__ desc0) {
+    __shared__ uint32_t wtot[16];
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint64_t carry = 0;  // words of the chunks before this block (uniform)
+    for (uint32_t base = 0; base < nfull; base += 1024) {
+        const uint32_t c = base + tid;
+        uint32_t cbits = 0;
+        if (c < nfull)
+            for (uint32_t k = 0; k < U; ++k) cbits += unit_bits[(uint64_t)c * U + k];
+        // a chunk has at most 2^24 * 12 bits, so 64 chunks' words fit 32 bits
+        const uint32_t words = c < nfull ? (cbits + 31) >> 5 : 0u;
+        const uint32_t incl = wave_incl_scan(words);
+        if (lane == 63) wtot[wave] = incl;
+        __syncthreads();
+        uint64_t before = carry, total = carry;
+        for (uint32_t w = 0; w < 16; ++w) {
+            const uint64_t t = wtot[w];
+            before += w < wave ? t : 0;
+            total += t;
+        }
+        if (c < nfull) {
+            const uint64_t cw = before + incl - words;
+            chunk_bits[c] = cbits;
+            cwo[c] = cw;
+            uint32_t off = 0;
+            for (uint32_t k = 0; k < U; ++k) {
+                const uint64_t u = (uint64_t)c * U + k;
+                const uint32_t b = unit_bits[u];
+                unit_bits[u] = off;
+                const uint64_t p = cw * 32 + off;
+                payload[p >> 5] = 0;
+                payload[(p + b - 1) >> 5] = 0;
+                off += b;
+            }
+        }
+        carry = total;
+        __syncthreads();  // wtot is read before the next block writes it
+    }
+    if (tid == 0) {
+        cwo[nfull] = carry;
+        st_desc(desc0, kDescInclusive | carry);
+    }
+}
+
+// Stores buffer words [i0, i1) to dst[i0 ..] (plain, non-temporal), lanes
+// spread over whole lines from the first 128-byte boundary on.
+__device__ __forceinline__ void store_words(const uint32_t *buf, uint32_t *dst, uint64_t dst_word, uint32_t i0,
+                                            uint32_t i1, uint32_t tid) {
+    if (i1 <= i0) return;
+    const uint32_t hd = (uint32_t)((32 - ((dst_word + i0) & 31)) & 31);
+    const uint32_t head = i0 + (hd < i1 - i0 ? hd : i1 - i0);
+    if (i0 + tid < head) __builtin_nontemporal_store(buf[i0 + tid], dst + i0 + tid);
+    for (uint32_t i = head + tid; i < i1; i += kUT) __builtin_nontemporal_store(buf[i], dst + i);
+}
+
+__global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void encode_placed_kernel(
+    const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint32_t U,
+    const uint32_t *__restrict__ unit_off, const uint64_t *__restrict__ cwo, uint32_t *__restrict__ payload,
+    uint32_t *__restrict__ sub_off) {
+    __shared__ UnitShared sh;
+    const uint32_t tid = threadIdx.x, lane = tid & 63;
+    const uint32_t wave = uniform(tid >> 6);
+    const uint32_t u = blockIdx.x;
+    const uint32_t c = u / U;
+    if (tid < 256) {
+        const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
+        sh.tab[tid] = ((uint32_t)reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid] << 16) | cbb[kOffLength + tid];
+    }
+    for (uint32_t i = tid; i < (kUBufW + 8) / 4; i += kUT) reinterpret_cast<uint4 *>(sh.buf)[i] = make_uint4(0, 0, 0, 0);
+    uint4 x[kUTiles];
+    const uint8_t *src = in + (uint64_t)u * kBigUnit + tid * 16;
+#pragma unroll
+    for (uint32_t r = 0; r < kUTiles; ++r) x[r] = load_stream16(src + r * kUTile);
+    // the unit's first bit in the payload
+    const uint64_t P = cwo[c] * 32 + unit_off[u];
+    __syncthreads();
+    TileGroups tg[kUTiles];
+    uint32_t ex[kUTiles];
+#pragma unroll
+    for (uint32_t r = 0; r < kUTiles; ++r) {
+        uint64_t g[4];
+        uint32_t ng[4];
+        asm volatile("" : "+v"(x[r].x), "+v"(x[r].y), "+v"(x[r].z), "+v"(x[r].w));
+        lane_groups(x[r], sh, g, ng);
+        const uint32_t bits = ng[0] + ng[1] + ng[2] + ng[3];
+        const uint32_t incl = wave_incl_scan(bits);
+        if (lane == 63) sh.wtot[r * kUW + wave] = incl;
+        ex[r] = incl - bits;
+        keep_groups(g, ng, tg[r]);
+    }
+    __syncthreads();
+    const uint32_t v = sh.wtot[lane];
+    const uint32_t incl = wave_incl_scan(v);
+    const uint32_t exs = incl - v;
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t p0 = (uint32_t)(uniform64(P) & 31);
+    const uint64_t w0 = uniform64(P) >> 5;
+    const uint32_t off = unit_off[u];
+    uint32_t pos[kUTiles];
+#pragma unroll
+    for (uint32_t r = 0; r < kUTiles; ++r)
+        pos[r] = (uint32_t)__builtin_amdgcn_readlane((int)exs, (int)(r * kUW + wave)) + ex[r];
+    // side index: a chunk has U * 256 sub-streams, unit u's run from u * 256
+    if ((lane & 15) == 0) {
+        uint32_t *so = sub_off + (uint64_t)u * (kBigUnit / kSub) + (tid >> 4);
+#pragma unroll
+        for (uint32_t r = 0; r < kUTiles; ++r) so[r * (kUTile / kSub)] = off + pos[r];
+    }
+    const uint32_t nw = (p0 + total + 31) >> 5;
+    uint32_t *dst = payload + w0;
+    if (nw <= kUBufW - 2) {
+#pragma unroll
+        for (uint32_t r = 0; r < kUTiles; ++r) place_tile(tg[r], p0 + pos[r], sh.buf);
+        __syncthreads();
+        // the unit's first and last word may hold a neighbour's bits
+        if (tid == 0) atomicOr(dst, sh.buf[0]);
+        if (tid == kUT - 1 && nw > 1) atomicOr(dst + nw - 1, sh.buf[nw - 1]);
+        store_words(sh.buf, dst, w0, 1, nw - 1, tid);
+    } else {
+        // more words than the buffer holds (data that does not compress):
+        // two halves of four tiles
+        constexpr uint32_t kHalf = kUTiles / 2;
+#pragma unroll
+        for (uint32_t r = 0; r < kHalf; ++r) place_tile(tg[r], p0 + pos[r], sh.buf);
+        __syncthreads();
+        const uint32_t fb = (p0 + (uint32_t)__builtin_amdgcn_readlane((int)exs, (int)(kHalf * kUW))) >> 5;
+        if (tid == 0) atomicOr(dst, sh.buf[0]);
+        store_words(sh.buf, dst, w0, 1, fb, tid);
+        const uint32_t carry = sh.buf[fb];
+        __syncthreads();
+        for (uint32_t i = tid; i <= fb + 2; i += kUT) sh.buf[i] = i == 0 ? carry : 0u;
+        __syncthreads();
+#pragma unroll
+        for (uint32_t r = kHalf; r < kUTiles; ++r) place_tile(tg[r], p0 + pos[r] - fb * 32, sh.buf);
+        __syncthreads();
+        if (tid == kUT - 1) atomicOr(dst + nw - 1, sh.buf[nw - 1 - fb]);
+        store_words(sh.buf, dst + fb, w0 + fb, 0, nw - 1 - fb, tid);
+    }
+}
+
 // Any chunk size: the counting pass and the packing pass each read the
 // chunk (the second read is served by the caches for moderate chunks).
 // A workgroup takes ticket t from counter `counter` (0 or 1) of workspace
@@ -917,7 +1106,27 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
         if (e != hipSuccess) return e;
     }
     const bool units = nfull * chunk >= (uint64_t)cus * 8 * kUTiles * kUTile && cus > 0;
-    if (chunk == 65536 && units) PC_ENC_UNIT(8);
+    uint64_t dbase = 0, cbase = 0;  // look-back index and chunk of the re-reading kernel's ticket 0
+    bool dset = false;
+    if (chunk > kBigUnit && chunk % kBigUnit == 0) {
+        if (nfull) {
+            // chunks of several 64 KiB units: count, scan, place (above)
+            const uint32_t U = chunk / kBigUnit;
+            const uint64_t nunits = nfull * U;
+            uint32_t *unit_bits = reinterpret_cast<uint32_t *>(ws + 1 + nc);
+            hipLaunchKernelGGL(encode_count_kernel, dim3((uint32_t)nunits), dim3(256), 0, stream, cb, in, unit_bits);
+            hipLaunchKernelGGL(encode_unit_scan_kernel, dim3(1), dim3(1024), 0, stream, unit_bits, U, (uint32_t)nfull,
+                               chunk_bits, cwo, payload, ws + 1);
+            hipLaunchKernelGGL(encode_placed_kernel, dim3((uint32_t)nunits), dim3(kUT), 0, stream, cb, in, U,
+                               unit_bits, cwo, payload, sub_off);
+            done = nfull;
+            // a short last chunk looks back to descriptor 0, which the scan
+            // published inclusive
+            dbase = 1;
+            cbase = nfull;
+            dset = true;
+        }
+    } else if (chunk == 65536 && units) PC_ENC_UNIT(8);
     else if (chunk == 32768 && units) PC_ENC_UNIT(4);
     else if (chunk == 16384 && units) PC_ENC_UNIT(2);
     else if (chunk == 65536) PC_ENC(1024, 4, 16392, 4);
@@ -932,13 +1141,17 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
     // chunk kernels (which take exactly `tickets` tickets from counter 0)
     // ticket t encodes chunk t + done - tickets; after the persistent unit
     // kernel (which may take extra tickets of counter 0) the tickets of
-    // counter 1 start at 0, look-back index tickets + t, chunk done + t
+    // counter 1 start at 0, look-back index tickets + t, chunk done + t;
+    // after the three launches of multi-unit chunks, ticket 0 of counter 0
+    // has look-back index 1 (descriptor 0 holds the full chunks' words)
     if (rest) {
-        const uint32_t dbase = counter ? (uint32_t)tickets : 0u;
-        const uint32_t cbase = counter ? (uint32_t)done : (uint32_t)(done - tickets);
+        if (!dset) {
+            dbase = counter ? tickets : 0u;
+            cbase = counter ? done : done - tickets;
+        }
         hipLaunchKernelGGL(encode_kernel_any, dim3((uint32_t)rest), dim3(kThreads), 0, stream, cb, in, n, chunk,
-                           (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws, counter, dbase, cbase, status,
-                           max_polls);
+                           (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws, counter, (uint32_t)dbase,
+                           (uint32_t)cbase, status, max_polls);
     }
 #undef PC_ENC
 #undef PC_ENC_UNIT

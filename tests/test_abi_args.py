@@ -95,3 +95,20 @@ def test_traffic_probe_args():
     assert lib.pc_traffic_probe(A, None, 64, None) == pc.PC_ERR_INVALID_ARG
     assert lib.pc_traffic_probe(A, A, 63, None) == pc.PC_ERR_INVALID_ARG
     assert lib.pc_traffic_probe(ODD, A, 64, None) == pc.PC_ERR_INVALID_ARG
+
+
+def test_workspace_of_multi_unit_chunks():
+    # chunks of several 64 KiB units keep one u32 per unit of the full chunks
+    for n, chunk in ((1 << 30, 1 << 17), ((1 << 30) + 5000, 1 << 20), (3 << 24, 1 << 24)):
+        nc = pc.pc_num_chunks(n, chunk)
+        units = (n // chunk) * (chunk // 65536)
+        assert pc.pc_encode_workspace_bytes(n, chunk) == 8 * (1 + nc) + 8 * ((units + 1) // 2)
+    assert pc.pc_encode_workspace_bytes(1 << 30, 65536) == 8 * (1 + (1 << 14))
+    assert pc.pc_encode_workspace_bytes(1 << 30, 3 * 65536 // 2) == 8 * (1 + pc.pc_num_chunks(1 << 30, 98304))
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_array():
+    # 2^37 bytes in 16 MiB chunks: 8192 chunks, but 2^21 unit counts
+    n, chunk = 1 << 37, 1 << 24
+    cap = pc.pc_max_payload_words(n, chunk)
+    assert lib.pc_encode_noalloc(A, A, n, chunk, A, cap, A, A, A, A, None) == pc.PC_ERR_CAPACITY

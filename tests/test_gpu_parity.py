@@ -159,6 +159,31 @@ def test_persistent_unit_path(chunk):
     assert torch.equal(out, x)
 
 
+@pytest.mark.parametrize("chunk", [1 << 17, 1 << 20, 1 << 24])
+def test_multi_unit_chunks(chunk):
+    """Chunks of several 64 KiB units (count, scan and place launches, units
+    joined mid-word with atomic ORs on the shared words), with a short last
+    chunk for the re-reading kernel, and 64 KiB runs of long codes (units
+    that go out in two halves) at a chunk's start, inside, and at its end;
+    compared in full with the oracle, and decoded back."""
+    n = (2 if chunk == 1 << 24 else 3) * chunk + 1000
+    dcb, obook = make_book(random_counts(5))
+    long_syms = np.flatnonzero(np.asarray(obook["lengths"]) >= 10).astype(np.uint8)
+    x_np = skewed(n, chunk + 1)
+    rng = np.random.default_rng(chunk)
+    U = chunk // 65536
+    for u in (0, U // 2 + 1, 2 * U - 1):  # whole units of long codes
+        x_np[u * 65536:(u + 1) * 65536] = rng.choice(long_syms, 65536)
+    say("multi-unit chunks: chunk", chunk, "n", n)
+    x, enc = gpu_encode(dcb, x_np, chunk)
+    want = coder.encode(x_np, obook["lengths"], obook["codes"], chunk, threads=16)
+    assert_same_stream(host(enc), want)
+    out, status = pc.pc_decode(dcb, enc)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(out, x)
+
+
 def skewed(n, seed):
     rng = np.random.default_rng(seed)
     return ((rng.zipf(1.4, n) * 37) % 256).astype(np.uint8)
