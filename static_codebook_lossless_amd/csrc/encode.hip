@@ -527,6 +527,7 @@ struct UnitShared {
     uint32_t tab[256];                 // code << 16 | length
     uint32_t wtot[kUTiles * kUW];      // per (tile, wave): bits
     uint32_t misc[4];                  // [0] ticket of this unit, [1] of the next, [2..3] its word offset
+    uint2 cmeta[2][kUTiles * kUW];     // per round (two in flight), chunk's first entry: (bits, first word)
     uint32_t buf[kUBufW + 8];
 };
 
@@ -565,21 +566,23 @@ __device__ __forceinline__ void place_tile(const TileGroups &tg, uint32_t p, uin
 }
 
 // The unit's look-back (one wave) and its chunks' metadata; the exclusive
-// word offset goes to sh.misc[2..3].
-template <int NC>
-__device__ __forceinline__ void unit_meta(UnitShared &sh, uint64_t *desc, uint32_t s, uint64_t words, uint32_t lane,
-                                          uint32_t max_polls, uint32_t *status, uint32_t *chunk_bits, uint64_t *cwo,
-                                          uint32_t c0, uint32_t num_chunks, const uint32_t (&cbits)[NC],
-                                          const uint32_t (&cw)[NC]) {
+// word offset goes to sh.misc[2..3].  The chunks' bit counts and first words
+// in the unit sit in sh.cmeta[slot] at each chunk's first entry (i % E == 0).
+template <uint32_t E>
+__device__ __forceinline__ void unit_meta(UnitShared &sh, uint32_t slot, uint64_t *desc, uint32_t s, uint64_t words,
+                                          uint32_t lane, uint32_t max_polls, uint32_t *status, uint32_t *chunk_bits,
+                                          uint64_t *cwo, uint32_t num_chunks) {
+    constexpr uint32_t NC = 64 / E;
     const uint64_t excl = lookback(desc, s, words, lane, max_polls, status, true);
+    const uint32_t c0 = s * NC;
+    if (lane % E == 0) {
+        const uint2 m = sh.cmeta[slot][lane];
+        chunk_bits[c0 + lane / E] = m.x;
+        cwo[c0 + lane / E] = excl + m.y;
+    }
     if (lane == 0) {
         sh.misc[2] = (uint32_t)excl;
         sh.misc[3] = (uint32_t)(excl >> 32);
-#pragma unroll
-        for (int k = 0; k < NC; ++k) {
-            chunk_bits[c0 + k] = cbits[k];
-            cwo[c0 + k] = excl + cw[k];
-        }
         if (c0 + NC == num_chunks) cwo[num_chunks] = excl + words;
     }
 }
@@ -604,12 +607,11 @@ __device__ __forceinline__ void store_unit(uint32_t *buf, uint32_t *dst, uint64_
     }
 }
 
-template <int TPC>  // tiles per chunk: 8, 4 or 2
+template <uint32_t E>  // (tile, wave) entries per chunk: 64, 32, 16, 8 or 4 (chunks of 64 .. 4 KiB)
 __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void encode_unit_kernel(
     const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint32_t num_chunks, uint32_t num_units,
     uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits, uint64_t *__restrict__ cwo,
     uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws, uint32_t *__restrict__ status, uint32_t max_polls) {
-    constexpr int NC = kUTiles / TPC;  // chunks per unit
     __shared__ UnitShared sh;
     const uint32_t tid = threadIdx.x;
     const uint32_t wave = uniform(tid >> 6);
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
     }
     // the unit placed in the buffer last round, still to be stored
     bool have_a = false;
-    uint32_t sa = 0, words_a = 0, cbits_a[NC], cw_a[NC];
+    uint32_t sa = 0, words_a = 0, slot = 0;  // slot: this round's half of sh.cmeta
     while (true) {
         // the lane index passes an opaque step each round, so that values
         // derived from it are recomputed rather than held (and spilled)
@@ -642,7 +644,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         const bool live = s < num_units;
         // ---- phase 1: lookups, groups, wave scans ----------------------
         TileGroups tg[kUTiles];
-        uint32_t ex[kUTiles];  // bits before the ln within its wave, per tile
+        uint32_t ex[kUTiles];  // bits before the lane within its wave, per tile
         if (live) {
 #pragma unroll
             for (uint32_t r = 0; r < kUTiles; ++r) {
@@ -663,36 +665,39 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         }
         __syncthreads();
         // ---- offsets: a scan over the 64 (tile, wave) totals -------------
-        uint32_t s_next = 0, words = 0, exs = 0;
-        uint32_t cbase[NC], cbits[NC], cw[NC], pos[kUTiles];
+        // lane i of every wave holds entry i = 8 r + w (tile r, wave w);
+        // chunk k of the unit is entries k E .. k E + E - 1 and starts on a
+        // new word (word cw of the unit's buffer)
+        uint32_t s_next = 0, words = 0, half_base = 0;
+        uint32_t pos[kUTiles];
         if (live) {
             s_next = uniform(sh.misc[1]);
             const uint32_t v = sh.wtot[ln];
             const uint32_t incl = wave_incl_scan(v);
-            exs = incl - v;
-            uint32_t cword = 0;
-#pragma unroll
-            for (int k = 0; k < NC; ++k) {
-                const int i0 = k * TPC * kUW, i1 = (k + 1) * TPC * kUW - 1;
-                cbase[k] = (uint32_t)__builtin_amdgcn_readlane((int)exs, i0);
-                cbits[k] = (uint32_t)__builtin_amdgcn_readlane((int)incl, i1) - cbase[k];
-                cw[k] = cword;
-                cword += (cbits[k] + 31) >> 5;
-            }
-            words = cword;
-            // the ln's first bit of tile r in the unit's buffer (chunk k
-            // of the unit starts on word cw[k])
+            const uint32_t exs = incl - v;
+            const uint32_t lead = ln & ~(E - 1);  // the chunk's first entry
+            const uint32_t cstart = (uint32_t)__shfl((int)exs, (int)lead);
+            const uint32_t cbits = (uint32_t)__shfl((int)incl, (int)(lead + E - 1)) - cstart;
+            const uint32_t cwords = ln == lead ? (cbits + 31) >> 5 : 0u;
+            const uint32_t wincl = wave_incl_scan(cwords);
+            const uint32_t cw = (uint32_t)__shfl((int)(wincl - cwords), (int)lead);
+            words = (uint32_t)__builtin_amdgcn_readlane((int)wincl, 63);
+            if (wave == 0 && ln == lead) sh.cmeta[slot][ln] = make_uint2(cbits, cw);
+            const uint32_t cwb = cw * 32;
+            const uint32_t base = cwb + exs - cstart;  // entry's first bit in the unit's buffer
+            half_base = (uint32_t)__builtin_amdgcn_readlane((int)base, (int)(kUTiles / 2 * kUW));
+            // the lane's first bit of tile r in the unit's buffer
 #pragma unroll
             for (uint32_t r = 0; r < kUTiles; ++r)
-                pos[r] = cw[r / TPC] * 32 + (uint32_t)__builtin_amdgcn_readlane((int)exs, (int)(r * kUW + wave)) -
-                         cbase[r / TPC] + ex[r];
-            // side index: every 256th symbol starts on a ln with
-            // ln % 16 == 0 (a chunk has TPC * 32 sub-streams, so the
-            // unit's run from s * 256)
+                pos[r] = (uint32_t)__builtin_amdgcn_readlane((int)base, (int)(r * kUW + wave)) + ex[r];
+            // side index: every 256th symbol starts on a lane with
+            // lane % 16 == 0 (a chunk has E * 4 sub-streams, so the unit's
+            // run from s * 256); entries are relative to their chunk
             if ((ln & 15) == 0) {
                 uint32_t *so = sub_off + (uint64_t)s * (kUTiles * kUTile / kSub) + (tl >> 4);
 #pragma unroll
-                for (uint32_t r = 0; r < kUTiles; ++r) so[r * (kUTile / kSub)] = pos[r] - cw[r / TPC] * 32;
+                for (uint32_t r = 0; r < kUTiles; ++r)
+                    so[r * (kUTile / kSub)] = pos[r] - (uint32_t)__builtin_amdgcn_readlane((int)cwb, (int)(r * kUW + wave));
             }
             if (wave == 0 && ln == 0) publish_count(desc, s, words);
         }
@@ -701,8 +706,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         // mostly published theirs)
         if (have_a) {
             if (wave == 0)
-                unit_meta(sh, desc, sa, words_a, ln, max_polls, status, chunk_bits, cwo, sa * NC, num_chunks, cbits_a,
-                          cw_a);
+                unit_meta<E>(sh, slot ^ 1u, desc, sa, words_a, ln, max_polls, status, chunk_bits, cwo, num_chunks);
             __syncthreads();
             const uint64_t at = unit_excl(sh);
             store_unit(sh.buf, payload + at, at, words_a, tl);
@@ -710,7 +714,6 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         // the buffer is clear and every wave has read the totals
         __syncthreads();
         if (!live) break;
-        const uint32_t c0 = s * NC;
         // the next unit's input is loaded while this one is placed; after
         // the last unit every lane reads the input's first 16 bytes (a
         // load on every path: a conditional one would keep the old values
@@ -729,16 +732,11 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
             have_a = true;
             sa = s;
             words_a = words;
-#pragma unroll
-            for (int k = 0; k < NC; ++k) {
-                cbits_a[k] = cbits[k];
-                cw_a[k] = cw[k];
-            }
         } else {
             // ---- a unit that does not fit the buffer (only data that does
             // not compress): its look-back now, then two halves of four
             // tiles (each fits) -------------------------------------------
-            if (wave == 0) unit_meta(sh, desc, s, words, ln, max_polls, status, chunk_bits, cwo, c0, num_chunks, cbits, cw);
+            if (wave == 0) unit_meta<E>(sh, slot, desc, s, words, ln, max_polls, status, chunk_bits, cwo, num_chunks);
             constexpr uint32_t kHalf = kUTiles / 2;
 #pragma unroll
             for (uint32_t r = 0; r < kHalf; ++r) place_tile(tg[r], pos[r], sh.buf);
@@ -746,9 +744,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
             const uint64_t excl = unit_excl(sh);
             // unit word fb holds the bits of both halves; whole words
             // before it go out, it moves to buf[0]
-            const uint32_t k = kHalf / TPC;
-            const uint32_t fb =
-                (cw[k] * 32 + (uint32_t)__builtin_amdgcn_readlane((int)exs, (int)(kHalf * kUW)) - cbase[k]) >> 5;
+            const uint32_t fb = half_base >> 5;
             for (uint32_t i = tl; i < fb; i += kUT) payload[excl + i] = sh.buf[i];
             const uint32_t carry = sh.buf[fb];
             __syncthreads();
@@ -764,6 +760,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
             have_a = false;
         }
         s = s_next;
+        slot ^= 1u;
     }
 }
 
@@ -1082,24 +1079,24 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
             tickets = nsup;                                                                                \
         }                                                                                               \
     } while (0)
-#define PC_ENC_UNIT(TPC)                                                                                   \
+#define PC_ENC_UNIT(E)                                                                                     \
     do {                                                                                                   \
-        const uint64_t nunits = nfull / (kUTiles / (TPC));                                                 \
+        const uint64_t nunits = nfull / (64 / (E));                                                        \
         uint64_t grid = 2 * (uint64_t)cus;                                                                 \
         if (grid > nunits) grid = nunits;                                                                  \
-        hipLaunchKernelGGL((encode_unit_kernel<TPC>), dim3((uint32_t)grid), dim3(kUT), 0, stream, cb, in,  \
+        hipLaunchKernelGGL((encode_unit_kernel<E>), dim3((uint32_t)grid), dim3(kUT), 0, stream, cb, in,    \
                            (uint32_t)nc, (uint32_t)nunits, payload, chunk_bits, cwo, sub_off, ws, status,  \
                            max_polls);                                                                     \
-        done = nunits * (kUTiles / (TPC));                                                                 \
+        done = nunits * (64 / (E));                                                                        \
         tickets = nunits;                                                                                  \
         counter = 1;                                                                                       \
     } while (0)
-    // 64, 32 and 16 KiB chunks: the persistent unit kernel once every
+    // 64 .. 4 KiB chunks: the persistent unit kernel once every
     // workgroup gets at least four units (it keeps two in flight; below
     // that the chunk kernels, which start all their workgroups at once, are
     // as fast or faster, measured)
     int cus = 0;
-    if (chunk == 65536 || chunk == 32768 || chunk == 16384) {
+    if (chunk <= 65536 && chunk >= 4096 && (chunk & (chunk - 1)) == 0) {
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1126,9 +1123,11 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
             cbase = nfull;
             dset = true;
         }
-    } else if (chunk == 65536 && units) PC_ENC_UNIT(8);
-    else if (chunk == 32768 && units) PC_ENC_UNIT(4);
-    else if (chunk == 16384 && units) PC_ENC_UNIT(2);
+    } else if (chunk == 65536 && units) PC_ENC_UNIT(64);
+    else if (chunk == 32768 && units) PC_ENC_UNIT(32);
+    else if (chunk == 16384 && units) PC_ENC_UNIT(16);
+    else if (chunk == 8192 && units) PC_ENC_UNIT(8);
+    else if (chunk == 4096 && units) PC_ENC_UNIT(4);
     else if (chunk == 65536) PC_ENC(1024, 4, 16392, 4);
     else if (chunk == 32768) PC_ENC(1024, 4, 16392, 2);
     else if (chunk == 16384) PC_ENC(1024, 4, 16392, 1);
