@@ -497,25 +497,27 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
 }
 
 // ---------------------------------------------------------------------------
-// Units of 64 KiB (1, 2 or 4 whole chunks of 64, 32 or 16 KiB), persistent
-// 512-lane workgroups, two per CU (128 registers per lane).  A unit is eight
-// tiles of 8 KiB; lane l of tile r owns its 16 symbols at r * 8192 + 16 l.
-//   phase 1: all eight tiles are already in registers (loaded during the
-//     previous unit); each tile's 16 (code, length) lookups become four
-//     groups of <= 48 bits, kept in registers, and a wave scan of the bit
-//     counts.  One barrier, then one wave scan over the 64 (tile, wave)
-//     totals gives every lane's bit offset in every tile, the chunks' bit
-//     counts and the unit's word count, which is published at once.
-//   phase 2: the groups are ORed into the LDS buffer at their offsets, with
-//     no barrier, and each tile's registers then take the next unit's input
-//     (its ticket was taken at the end of phase 1), so the loads of one unit
-//     are in flight while the next is packed.  Wave 0 then walks back over
-//     the earlier units' descriptors; as every unit publishes its count
-//     before it packs, the walk mostly finds its predecessors published.
-//   the unit is stored once, coalesced, at its final offset.
+// Units of 64 KiB (1 to 64 whole chunks of 64 .. 1 KiB), persistent 512-lane
+// workgroups, two per CU (128 registers per lane), taking units by ticket.
+// A unit is eight tiles of 8 KiB; lane l of tile r owns its 16 symbols at
+// r * 8192 + 16 l; entry 8 r + w is wave w's part of tile r (1 KiB), and a
+// chunk is E consecutive entries.  One round, with unit B's input in
+// registers and unit A (the previous one) placed in the LDS buffer:
+//   phase 1: per tile, 16 (code, length) lookups become four groups of
+//     <= 48 bits, kept in registers, and a wave scan of the bit counts; the
+//     next unit's ticket is taken.
+//   offsets: one barrier, then a wave scan over the 64 entry totals and one
+//     over the chunks' words give every lane's bit offset in every tile, the
+//     chunks' bit counts and first words, and B's word count, which is
+//     published at once.
+//   A's look-back (wave 0; A's count was published a round ago, so its
+//     predecessors have mostly published theirs), then A is stored,
+//     coalesced, at its final offset, clearing the buffer.
+//   phase 2: B's groups are ORed into the buffer with no barrier; each
+//     tile's registers then take the next unit's input for that tile.
 // A unit whose words would not fit the buffer (only data that does not
-// compress) does its look-back first and is placed and stored in two halves
-// of four tiles from the same registers.
+// compress) does its look-back at once and is placed and stored in two
+// halves of four tiles from the same registers.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kUT = 512;                  // lanes
 constexpr uint32_t kUW = kUT / 64;             // waves
@@ -607,7 +609,7 @@ __device__ __forceinline__ void store_unit(uint32_t *buf, uint32_t *dst, uint64_
     }
 }
 
-template <uint32_t E>  // (tile, wave) entries per chunk: 64, 32, 16, 8 or 4 (chunks of 64 .. 4 KiB)
+template <uint32_t E>  // (tile, wave) entries per chunk: 64 .. 1 (chunks of 64 .. 1 KiB)
 __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void encode_unit_kernel(
     const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint32_t num_chunks, uint32_t num_units,
     uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits, uint64_t *__restrict__ cwo,
@@ -1091,12 +1093,12 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
         tickets = nunits;                                                                                  \
         counter = 1;                                                                                       \
     } while (0)
-    // 64 .. 4 KiB chunks: the persistent unit kernel once every
+    // 64 .. 1 KiB chunks: the persistent unit kernel once every
     // workgroup gets at least four units (it keeps two in flight; below
     // that the chunk kernels, which start all their workgroups at once, are
     // as fast or faster, measured)
     int cus = 0;
-    if (chunk <= 65536 && chunk >= 4096 && (chunk & (chunk - 1)) == 0) {
+    if (chunk <= 65536 && chunk >= 1024 && (chunk & (chunk - 1)) == 0) {
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1128,6 +1130,8 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
     else if (chunk == 16384 && units) PC_ENC_UNIT(16);
     else if (chunk == 8192 && units) PC_ENC_UNIT(8);
     else if (chunk == 4096 && units) PC_ENC_UNIT(4);
+    else if (chunk == 2048 && units) PC_ENC_UNIT(2);
+    else if (chunk == 1024 && units) PC_ENC_UNIT(1);
     else if (chunk == 65536) PC_ENC(1024, 4, 16392, 4);
     else if (chunk == 32768) PC_ENC(1024, 4, 16392, 2);
     else if (chunk == 16384) PC_ENC(1024, 4, 16392, 1);

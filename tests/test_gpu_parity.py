@@ -127,7 +127,7 @@ def test_stream_1g_full_size():
     assert int(host(enc)["chunk_bits"].astype(np.int64).sum()) == cb.coded_bits(xc, obook["lengths"])
 
 
-@pytest.mark.parametrize("chunk", [65536, 32768, 16384, 8192, 4096])
+@pytest.mark.parametrize("chunk", [65536, 32768, 16384, 8192, 4096, 2048, 1024])
 def test_persistent_unit_path(chunk):
     """Inputs large enough for the persistent 64 KiB-unit encoder (four
     units per workgroup at two workgroups per CU), with whole chunks and a
