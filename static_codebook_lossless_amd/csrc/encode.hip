@@ -1056,17 +1056,22 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
                        ws_words, cwo, n == 0 ? 1 : 0, status);
     if (n == 0) return hipGetLastError();
     const uint64_t nfull = n / chunk;  // chunks of exactly `chunk` symbols
-    // Full chunks go to workgroups of NT tiles (TPC tiles per chunk, so
-    // NT / TPC consecutive chunks and one look-back per workgroup); the
-    // full chunks left over and a short last chunk go to the re-reading
-    // kernel, launched after them, so their look-backs find every
-    // predecessor finished.  The 1024-lane kernels hold 64K symbols per
-    // workgroup; the LDS output buffer holds them at 8 bits per symbol plus
-    // the padding words between chunks and the 64-bit margin of the fit
-    // test (two such workgroups fit a CU).  4K and 8K symbol chunks take
-    // 256-lane workgroups of 32K symbols when there are many of them, else
-    // one chunk per workgroup, so that a small input still spreads over the
-    // CUs (the 1-chunk buffers hold 12 bits per symbol).
+    // Full chunks go to one of three launches, and the full chunks left
+    // over and a short last chunk to the re-reading kernel, launched after
+    // it, so that their look-backs find every predecessor finished:
+    //   - power-of-two chunks of 1 .. 64 KiB on large inputs: the persistent
+    //     unit kernel (64 KiB units of whole chunks);
+    //   - multiples of 64 KiB above it: count, scan and place launches;
+    //   - otherwise 4 .. 64 KiB chunks: workgroups of NT tiles (TPC tiles per
+    //     chunk, so NT / TPC consecutive chunks and one look-back per
+    //     workgroup).  The 1024-lane kernels hold 64K symbols per
+    //     workgroup; the LDS output buffer holds them at 8 bits per symbol
+    //     plus the padding words between chunks and the 64-bit margin of the
+    //     fit test (two such workgroups fit a CU).  4K and 8K symbol chunks
+    //     take 256-lane workgroups of 32K symbols when there are many of
+    //     them, else one chunk per workgroup, so that a small input still
+    //     spreads over the CUs (the 1-chunk buffers hold 12 bits per symbol).
+    // Other chunk sizes go to the re-reading kernel whole.
     constexpr uint64_t kManySmall = 8192;
     uint64_t done = 0, tickets = 0;  // chunks and look-back indices of the multi-chunk launch
     uint32_t counter = 0;            // the ticket counter of the re-reading kernel
