@@ -5,36 +5,37 @@
 // Lossless Compression of e4m3", abstract, blames bit-sequential tree walks
 // for slow Huffman decoding; here every codeword costs one table lookup).
 //
-// A "group" is 256 consecutive sub-streams (one per lane of a 256-lane
-// workgroup); its payload is one contiguous span of words.  Workgroups are
-// persistent and walk the groups with a stride of the grid size.  While a
-// workgroup decodes group k out of LDS, the loads of group k+1 (its
-// container entries, then its payload span into registers, one 16-byte
-// load per lane after each of the 16 steps of the first 128 symbols; the
-// span's entries come one group earlier still) are in flight, so HBM
-// latency is hidden behind decoding.  Per group:
-//   1. the staged span sits in LDS as contiguous words (a span starts on a
-//      64-word boundary);
-//   2. per lane and per 8 symbols: fetch 4 words around the current bit,
-//      funnel them into a 96-bit window (>= 96 valid bits), then 8 times:
-//      read the 32-bit table entry ((18 - length) | symbol << 8) of the 12
-//      bits at the current position, take the next entry's offset from the
-//      unadvanced window shifted by the entry, and advance the window with
-//      funnel shifts (v_alignbit) by the entry + 14 (lut32_step8);
-//   3. once the group is decoded, its output goes out through the free
-//      staging rows, half a sub-stream at a time, so that every store
-//      instruction writes whole 128-byte lines (store_group);
-//   4. the sub-stream must end exactly at the next sub-stream's first bit (or
+// A "group" is 256 consecutive sub-streams, one per lane of a 256-lane
+// workgroup; three workgroups share a CU.  Workgroups are persistent and walk
+// the groups with a stride of the grid size.  A group is decoded in two
+// halves of 128 symbols per lane, each out of an LDS segment of 40 words per
+// lane: the first half from the 40 words that start at the word holding the
+// sub-stream's first bit, the second from the 40 words that end at the word
+// holding its last bit.  Both start words are known from the side index
+// before the group is decoded, so each half's segments are loaded (one
+// 16-byte load per lane and decode step, consecutive lanes reading
+// consecutive quads of a segment) while the previous half decodes, and HBM
+// latency stays hidden.  A half fits its segment up to ~9.8 bits per
+// symbol; a group where some half does not is decoded again from global
+// memory (decode_group_global).  Per half and lane:
+//   1. per 8 symbols: fetch 4 words around the current bit, funnel them into
+//      a 96-bit window (>= 96 valid bits), then 8 times: read the 16-bit
+//      table entry ((19 - length) | symbol << 8) of the 12 bits at the
+//      current position, take the next entry's offset from the unadvanced
+//      window shifted by the entry, and advance the window with funnel
+//      shifts (v_alignbit) by the entry + 13 (lut16_step8, lut16_step8_fast);
+//   2. once the group is decoded, its output goes out through the segment
+//      area, half a sub-stream at a time, so that every store instruction
+//      writes whole 128-byte lines (store_group);
+//   3. the sub-stream must end exactly at the next sub-stream's first bit (or
 //      at chunk_bits); any mismatch sets *status = PC_ERR_CORRUPT.
-// A group whose span does not fit the LDS budget (above 7.9 bits per symbol:
-// data the code does not fit), and a last group that is not full, are
-// leftovers: after its staged groups, each workgroup decodes its share of
-// them straight from global memory.  The QLC variant replaces the 12-bit
-// table with the page's own decoder: a 3-bit area number, that area's
-// fixed-width index, and the 256-entry rank -> symbol table.  Its per-area
-// widths and first ranks sit in registers (looked up with v_perm), so the
-// decoding chain holds no memory read; only the rank -> symbol read, beside
-// the chain, goes to LDS.
+// A last group that is not full is a leftover: after its full groups, each
+// workgroup decodes its share of them straight from global memory.  The QLC
+// variant replaces the 12-bit table with the page's own decoder: a 3-bit
+// area number, that area's fixed-width index, and the 256-entry rank ->
+// symbol table.  Its per-area widths and first ranks sit in registers
+// (looked up with v_perm), so the decoding chain holds no memory read; only
+// the rank -> symbol read, beside the chain, goes to LDS.
 #include <atomic>
 
 #include "pc_internal.h"
@@ -43,19 +44,35 @@ namespace pc {
 namespace {
 
 constexpr uint32_t kThreads = 256;
-constexpr uint32_t kRow = 64;  // a staged span starts on a multiple of 64 words
-// Staged span: up to 16256 words of payload, a group at 7.9 bits per symbol
-// from a 64-word-aligned start (16 x 16 B per lane in flight), plus 4 spare
-// words for the window reads at its end, beside the 16 KiB table, with two
-// workgroups in a CU's LDS.
-constexpr uint32_t kLutBytes = 16384;
-constexpr uint32_t kPrefetch = 16;
-constexpr uint32_t kStageWords = 16256;
-constexpr uint32_t kStageBytes = (kStageWords + 4) * 4;
-constexpr uint32_t kGroupsPerCU = 2;
-static_assert(kStageWords <= kPrefetch * 4 * kThreads, "prefetch covers the staged span");
-// static LDS: the tables and the leftover list (below)
-static_assert(2 * (kLutBytes + 272 + kStageBytes) <= 160 * 1024, "two workgroups per CU");
+// Each sub-stream is staged in two segments of kSlotData words, one for its
+// first 128 symbols and one for its last 128.  Segment j of a group sits at
+// word 41 j of the segment area, so lanes reading the same word of their own
+// segments hit 32 different LDS banks.
+constexpr uint32_t kSlotWords = 41;            // segment stride in LDS (odd: 32 banks)
+constexpr uint32_t kSlotData = kSlotWords - 1;  // words staged per segment: whole 16-byte quads
+constexpr uint32_t kSlotBits = kSlotData * 32;
+constexpr uint32_t kSegQuads = kSlotData / 4;  // 16-byte loads per segment, by consecutive lanes
+constexpr uint32_t kSetLoads = kSegQuads;
+static_assert(kSlotData % 4 == 0 && kSlotWords % 2 == 1, "whole quads, odd stride");
+constexpr uint32_t kLutBytes = 8192;
+constexpr uint32_t kLutOff = 19;  // entry = (19 - length) | symbol << 8
+constexpr uint32_t kLutMask = 0x1FFE;
+constexpr uint32_t kGroupsPerCU = 3;
+// LDS layout (bytes): the table, the two segment-start tables (this group's
+// second halves, the next group's first halves), the leftover list and the
+// group-failure flag, then the slots (16-byte aligned: the output transpose
+// reuses them) and 4 spare words for window reads past the last slot.
+constexpr uint32_t kOffStartsA = kLutBytes;
+constexpr uint32_t kOffStartsB = kOffStartsA + 4 * kThreads;
+constexpr uint32_t kOffLeft = kOffStartsB + 4 * kThreads;
+constexpr uint32_t kOffFlag = kOffLeft + 264;
+constexpr uint32_t kOffSlots = kOffLeft + 272;
+constexpr uint32_t kLdsBytes = kOffSlots + (kThreads * kSlotWords + 4) * 4;
+static_assert(kOffSlots % 16 == 0, "slots hold 16-byte quads for the output transpose");
+static_assert(kThreads * kSlotWords * 4 >= 4 * 8192, "the output transpose fits the slots");
+// three workgroups per CU, with room for an LDS allocation granularity of
+// 512 or 1280 bytes
+static_assert(3 * ((kLdsBytes + 1279) / 1280 * 1280) <= 160 * 1024, "three workgroups per CU");
 
 __device__ __forceinline__ void flag_corrupt(uint32_t *status) {
     atomicCAS(status, 0u, (uint32_t)PC_ERR_CORRUPT);
@@ -64,8 +81,8 @@ __device__ __forceinline__ void flag_corrupt(uint32_t *status) {
 // Payload word sources.  Indices are clamped so that corrupt positions never
 // read outside the staged words or the payload.  fetch4 reads words a .. a+3;
 // fetch4m reads words q-1 .. q+2 (the window of the table decoder, see
-// lut32_step8; word -1 of the staged span is the LDS word before it, read but
-// never used, as are words past the span).
+// lut16_step8; word -1 of a segment is the LDS word before it, read but
+// never used, as are words past the segment).
 struct LdsWords {
     const uint32_t *w;
     uint32_t last;  // last staged word (relative)
@@ -80,7 +97,7 @@ struct LdsWords {
         // q = last + 1 is a lane whose remaining bits all lie in the last
         // word (read as word q - 1); the spare words after the span keep the
         // reads of q .. q + 2 inside the allocation
-        q = q <= last ? q : last + 1;
+        q = min(q, last + 1);
         const uint32_t *p = w + q - 1;
         v[0] = p[0];
         v[1] = p[1];
@@ -104,7 +121,7 @@ struct GlobalWords {
 };
 
 struct Tables {
-    const uint32_t *lut;  // LDS: 4096 x ((18 - length) | symbol << 8), 0 = no codeword
+    const uint32_t *lut;  // LDS: 4096 x u16 ((19 - length) | symbol << 8), 0 = no codeword
     const uint8_t *sym;   // LDS (QLC mode): symbol of rank r for r < 256, 0 up to 1023
     // QLC mode, one byte per area a (a = 0..3 in *_lo, 4..7 in *_hi), read
     // with v_perm, so that no table on the decoding chain sits in memory:
@@ -120,7 +137,7 @@ struct Tables {
 };
 
 // Whether a sub-stream met a bit pattern that is no codeword: LUT mode keeps
-// the least table entry read (a codeword's entry is at least 6, "no
+// the least table entry read (a codeword's entry is at least 7, "no
 // codeword" is 0), QLC mode the largest window seen.
 template <int MODE>
 __device__ __forceinline__ uint32_t no_invalid_yet() { return MODE == kDecodeLut12 ? ~0u : 0u; }
@@ -130,15 +147,15 @@ __device__ __forceinline__ bool saw_invalid(uint32_t bad, const Tables &t) {
     return MODE == kDecodeLut12 ? bad == 0 : (t.qlc_check && bad >= t.qlc_lim);
 }
 
-// Table decoder with one 32-bit entry per 12-bit peek: (18 - length) in the
+// Table decoder with one 16-bit entry per 12-bit peek: (19 - length) in the
 // low 5 bits (0 = no codeword), the symbol in byte 1.  The next entry's byte
 // offset comes from the window before it is advanced: the 12 bits after a
-// codeword of length len start len bits into h, so (h >> (18 - len)) &
-// 0x3FFC is four times their value; the window's funnel shifts (by 32 - len
-// = entry + 14 in the low 5 bits) run beside the next table read.  Per
-// symbol the chain of dependent instructions is one LDS read, one shift and
-// one mask (32-bit LDS reads of random entries also run at about twice the
-// rate of 16-bit ones, measured).  The bit position is kept negated (npos =
+// codeword of length len start len bits into h, so (h >> (19 - len)) &
+// 0x1FFE is twice their value; the window's funnel shifts (by 32 - len =
+// entry + 13 in the low 5 bits) run beside the next table read.  Per symbol
+// the chain of dependent instructions is one LDS read, one shift and one
+// mask.  The 8 KiB table leaves room for three workgroups' segments per CU.
+// The bit position is kept negated (npos =
 // -pos, mod 2^32): the window is the 96 bits from pos, funnelled from the
 // words q-1 .. q+2 with q = (pos + 31) / 32 by v_alignbit with shift npos (its
 // low 5 bits are (32 - pos % 32) % 32; pos % 32 == 0 shifts by 0 and takes
@@ -147,26 +164,26 @@ __device__ __forceinline__ bool saw_invalid(uint32_t bad, const Tables &t) {
 // variant only) consume nothing.  Returns the 8 symbols packed little-endian
 // in o0, o1.
 template <bool MASKED, bool CHECK, class Src>
-__device__ __forceinline__ void lut32_step8(const Src &src, uint32_t &npos, uint32_t &bad, const uint32_t *lut,
+__device__ __forceinline__ void lut16_step8(const Src &src, uint32_t &npos, uint32_t &bad, const uint32_t *lut,
                                             uint32_t k0, uint32_t lim, uint32_t &o0, uint32_t &o1) {
     uint32_t w[4];
     src.fetch4m((31u - npos) >> 5, w);
     uint32_t h = __builtin_amdgcn_alignbit(w[0], w[1], npos);
     uint32_t m = __builtin_amdgcn_alignbit(w[1], w[2], npos);
     uint32_t l = __builtin_amdgcn_alignbit(w[2], w[3], npos);
-    uint32_t a = (h >> 18) & 0x3FFC;
+    uint32_t a = (h >> kLutOff) & kLutMask;
     uint32_t e[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const bool masked = MASKED && k0 + k >= lim;
-        uint32_t ek = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(lut) + a);
+        uint32_t ek = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(lut) + a);
         if (CHECK) {
             const uint32_t c = masked ? ~0u : ek;
             bad = bad < c ? bad : c;
         }
-        if (masked) ek = (ek & 0xFF00u) | 18u;  // length 0: the window is kept
-        if (k < 7) a = (h >> (ek & 31)) & 0x3FFC;
-        const uint32_t s = ek + 14;  // 32 - length in the low 5 bits (32: masked, no advance)
+        if (masked) ek = (ek & 0xFF00u) | kLutOff;  // length 0: the window is kept
+        if (k < 7) a = (h >> (ek & 31)) & kLutMask;
+        const uint32_t s = ek + (32 - kLutOff);  // 32 - length in the low 5 bits (32: masked, no advance)
         if (k < 7) {
             const uint32_t h2 = __builtin_amdgcn_alignbit(h, m, s);
             const uint32_t m2 = __builtin_amdgcn_alignbit(m, l, s);
@@ -179,9 +196,9 @@ __device__ __forceinline__ void lut32_step8(const Src &src, uint32_t &npos, uint
         }
         e[k] = ek;
     }
-    // each low byte is 18 - length (<= 17): four of them sum below 256
+    // each low byte is 19 - length (<= 18): four of them sum below 256
     const uint32_t s0 = (e[0] + e[1] + e[2] + e[3]) & 0xFF, s1 = (e[4] + e[5] + e[6] + e[7]) & 0xFF;
-    npos += s0 + s1 - 8 * 18;  // -(bits consumed); masked entries count 18, i.e. nothing
+    npos += s0 + s1 - 8 * kLutOff;  // -(bits consumed); masked entries count 19, i.e. nothing
     o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
     o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
     // pack and check here: left to the scheduler, the packing sinks towards
@@ -189,6 +206,54 @@ __device__ __forceinline__ void lut32_step8(const Src &src, uint32_t &npos, uint
     // all eight entries of every step alive until then
     asm volatile("" : "+v"(o0), "+v"(o1));
     if (CHECK) asm volatile("" : "+v"(bad));
+}
+
+// The same decoder for a complete code (no "no codeword" entries) and all 8
+// symbols owed, with the window's word index q carried from step to step:
+// the next step's q is taken from the sum of the first 7 entries before the
+// 8th arrives, so the chain from the 8th entry to the next window read is a
+// subtract, a clamp, a shift and an address.  basem4 is the LDS byte address
+// of the lane's words minus 4 (the window starts at word q - 1).
+typedef const __attribute__((address_space(3))) uint32_t lds_u32;
+
+__device__ __forceinline__ void lut16_step8_fast(uint32_t basem4, uint32_t qlim, uint32_t &npos, uint32_t &q,
+                                                 const uint32_t *lut, uint32_t &o0, uint32_t &o1) {
+    lds_u32 *p = (lds_u32 *)(size_t)(basem4 + (min(q, qlim) << 2));
+    const uint32_t w0 = p[0], w1 = p[1], w2 = p[2], w3 = p[3];
+    uint32_t h = __builtin_amdgcn_alignbit(w0, w1, npos);
+    uint32_t m = __builtin_amdgcn_alignbit(w1, w2, npos);
+    uint32_t l = __builtin_amdgcn_alignbit(w2, w3, npos);
+    uint32_t a = (h >> kLutOff) & kLutMask;
+    const uint32_t K = 31u - npos + 8 * kLutOff;
+    const uint8_t *lb = reinterpret_cast<const uint8_t *>(lut);
+    uint32_t ecur = *reinterpret_cast<const uint16_t *>(lb + a);
+    uint32_t e[8];
+    uint32_t T = 0, K6 = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t ek = ecur;
+        if (k < 7) {
+            a = (h >> (ek & 31)) & kLutMask;
+            ecur = *reinterpret_cast<const uint16_t *>(lb + a);
+            const uint32_t s = ek + (32 - kLutOff);
+            h = __builtin_amdgcn_alignbit(h, m, s);
+            m = __builtin_amdgcn_alignbit(m, l, s);
+            l = __builtin_amdgcn_alignbit(l, 0u, s);
+            T += ek;
+        }
+        if (k == 6) {
+            // low bytes are 19 - length <= 18: their sum never carries out of byte 0
+            K6 = K - (T & 0xFF);
+            asm volatile("" : "+v"(K6));
+        }
+        e[k] = ek;
+    }
+    // (31 - npos') / 32 for npos' = npos + sum(19 - length) - 8 * 19
+    q = (K6 - (e[7] & 0xFF)) >> 5;
+    npos += ((T + e[7]) & 0xFF) - 8 * kLutOff;
+    o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
+    o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
+    asm volatile("" : "+v"(o0), "+v"(o1));
 }
 
 // QLC decoder, 8 symbols from the 96-bit window (h, m, l); returns them
@@ -235,7 +300,7 @@ template <int MODE, bool MASKED, bool CHECK, class Src>
 __device__ __forceinline__ void step8(const Src &src, uint32_t &pos, uint32_t &bad, const Tables &t, uint32_t k0,
                                       uint32_t lim, uint32_t &o0, uint32_t &o1) {
     if (MODE == kDecodeLut12) {  // pos holds -position here
-        lut32_step8<MASKED, CHECK>(src, pos, bad, t.lut, k0, lim, o0, o1);
+        lut16_step8<MASKED, CHECK>(src, pos, bad, t.lut, k0, lim, o0, o1);
     } else {
         uint32_t w[4];
         src.fetch4(pos >> 5, w);
@@ -297,7 +362,6 @@ __device__ __forceinline__ uint32_t vgpr_copy(uint32_t v) {
 // is decoded, see store_group).
 constexpr uint32_t kHalf = kSub / 2;
 constexpr uint32_t kHalfWords = kHalf / 4;
-static_assert(kPrefetch == kHalf / 8, "one prefetch load per step of a half");
 
 // side(q) runs after step q (8 symbols) of the 16: the memory instructions
 // of a group are spread over its decode steps, where the wave mostly waits
@@ -307,18 +371,29 @@ template <int MODE, bool CHECK, class Side>
 __device__ __forceinline__ uint32_t decode_half(const LdsWords &src, uint32_t pos, const Tables &t, uint32_t &bad,
                                                 uint32_t (&o)[kHalfWords], Side &&side) {
     pos = to_step_pos<MODE>(pos);
+    if (MODE == kDecodeLut12 && !CHECK) {
+        const uint32_t basem4 = (uint32_t)(size_t)(lds_u32 *)src.w - 4u;
+        uint32_t wq = (31u - pos) >> 5;
 #pragma unroll
-    for (uint32_t q = 0; q < kHalf / 8; ++q) {
-        step8<MODE, false, CHECK>(src, pos, bad, t, 0, kHalf, o[2 * q], o[2 * q + 1]);
-        side(q);
-        asm volatile("" ::: "memory");  // the side work stays at this step
+        for (uint32_t q = 0; q < kHalf / 8; ++q) {
+            lut16_step8_fast(basem4, src.last + 1, pos, wq, t.lut, o[2 * q], o[2 * q + 1]);
+            side(q);
+            asm volatile("" ::: "memory");  // the side work stays at this step
+        }
+    } else {
+#pragma unroll
+        for (uint32_t q = 0; q < kHalf / 8; ++q) {
+            step8<MODE, false, CHECK>(src, pos, bad, t, 0, kHalf, o[2 * q], o[2 * q + 1]);
+            side(q);
+            asm volatile("" ::: "memory");  // the side work stays at this step
+        }
     }
     return to_step_pos<MODE>(pos);
 }
 
 // A group's output goes out through LDS, half a sub-stream (128 bytes per
 // lane) at a time: each wave writes its lanes' 8 quads into its own 8 KiB
-// of the free staging rows, then reads them back so that every store
+// of the segment area, then reads them back so that every store
 // instruction writes eight whole 128-byte lines (8 lanes per line) instead of
 // 16 bytes into each of 64 lines.  Quad q of lane l sits at slot
 // l * 8 + (q ^ (l % 8)).
@@ -415,18 +490,6 @@ __device__ __forceinline__ void span_bits(SpanEntries e, uint64_t &a, uint64_t &
     b = e.w_next * 32 + (e.has_next ? e.off_next : 0u);
 }
 
-// Per-lane form (each lane may hold a different group's entries).
-__device__ __forceinline__ void span_words_lane(const SpanEntries &e, uint64_t payload_words, uint64_t &lo,
-                                                uint64_t &hi) {
-    uint64_t a, b;
-    span_bits(e, a, b);
-    lo = a >> 5;
-    hi = (b + 31) >> 5;
-    if (lo > payload_words) lo = payload_words;
-    if (hi > payload_words) hi = payload_words;
-    if (hi < lo) hi = lo;
-}
-
 __device__ __forceinline__ void span_words(const SpanEntries &e, uint64_t payload_words, uint64_t &lo, uint64_t &hi) {
     uint64_t a, b;
     span_bits(e, a, b);
@@ -437,64 +500,78 @@ __device__ __forceinline__ void span_words(const SpanEntries &e, uint64_t payloa
     if (hi < lo) hi = lo;
 }
 
-// Prefetch of a staged span into registers: one 16-byte load per quad of
-// words, unconditional and branch-free (control flow here would make the
-// compiler's wait counting conservative for the whole loop).  Quad indices
-// are clamped to the payload's last whole quad (the kernel runs only when
-// there is one); quads past it, or of a span too large to stage, are never
-// staged.  The up to 3 words after the last whole quad are read while
-// staging, by the one lane that needs them.  Nothing is read at or past
-// payload_words.
-struct Prefetch {
-    uint4 q[kPrefetch];
+// Segment loads.  A set: the first-half (or second-half) segments of a
+// group's 256 sub-streams, one start word per segment (relative to the
+// group's base word) in an LDS table.  The set's 2560 16-byte quads are
+// loaded by the 256 lanes in turn, 10 loads per lane, one per decode step,
+// unconditional and branch-free (control flow here would make the
+// compiler's wait counting conservative for the whole loop).  Quads are
+// 4-byte aligned (a segment starts at any word).  Start words are clamped
+// so that nothing at or past payload_words is read: a quad clamped back to
+// the payload's last four words is written to the segment at its true
+// position, so the words before the end stay right.
+struct SegFetch {
+    uint4 q[kSegQuads];
 };
 
-// The payload as the prefetch sees it: a global pointer passed through an
+// Quad k of a set's loads by lane tid: load tid + 256 k of the set, i.e.
+// quad part_of of segment seg_of (consecutive lanes read consecutive quads
+// of a segment, so one load instruction touches few 128-byte lines).
+__device__ __forceinline__ uint32_t seg_of(uint32_t k, uint32_t tid) { return (tid + kThreads * k) / kSegQuads; }
+__device__ __forceinline__ uint32_t part_of(uint32_t k, uint32_t tid) { return (tid + kThreads * k) % kSegQuads; }
+
+typedef const __attribute__((address_space(1))) uint32_t gword;
+typedef uint32_t u32x4w __attribute__((ext_vector_type(4), aligned(4)));
+typedef const __attribute__((address_space(1))) u32x4w gquadw;
+
+// The payload as the loads see it: a global pointer passed through an
 // empty asm, so that the compiler no longer knows that nothing writes the
 // words and keeps each load at the decode step it is issued at (loads of
 // memory known to be read-only are moved freely, and end up together).
-typedef const __attribute__((address_space(1))) u32x4 gquad;
-
-__device__ __forceinline__ gquad *opaque_quads(const uint32_t *payload) {
-    gquad *p = (gquad *)payload;
-    asm volatile("" : "+s"(p));
-    return p;
+__device__ __forceinline__ gword *opaque_words(const uint32_t *p) {
+    gword *g = (gword *)p;
+    asm volatile("" : "+s"(g));
+    return g;
 }
 
-// Quad k of lane tid of the span [lo, hi): quads past the span's last one
-// (or the payload's last whole one) read that quad again, so lanes with no
-// quad of their own add no traffic.
-__device__ __forceinline__ uint64_t last_quad(uint64_t lo, uint64_t hi, uint64_t payload_words) {
-    const uint64_t q0 = (lo & ~(uint64_t)(kRow - 1)) / 4;
-    uint64_t qe = (hi + 3) / 4;  // one past the span's last quad
-    if (qe <= q0) qe = q0 + 1;
-    if (qe > payload_words / 4) qe = payload_words / 4;
-    return qe - 1;
+// Load k of a set (k = 0..9); `start` is the start of the segment quad k
+// belongs to (read from the table a step earlier).
+__device__ __forceinline__ void seg_fetch(SegFetch &f, uint32_t k, uint32_t start, gword *gb, uint32_t pwr,
+                                          uint32_t tid) {
+    const uint32_t r = min(start + 4 * part_of(k, tid), pwr - 4);
+    const u32x4w v = *(gquadw *)((const __attribute__((address_space(1))) uint8_t *)gb + (r << 2));
+    f.q[k] = make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void prefetch_quad(Prefetch &pf, uint32_t k, gquad *payload, uint64_t lo,
-                                              uint64_t q_last, uint32_t tid) {
-    const uint64_t q = (lo & ~(uint64_t)(kRow - 1)) / 4 + tid + k * kThreads;
-    const u32x4 v = payload[q < q_last ? q : q_last];
-    pf.q[k] = make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ void issue_prefetch(Prefetch &pf, gquad *payload, uint64_t lo, uint64_t q_last,
-                                               uint32_t tid) {
+// The set's words into the segment area (every lane's loads are complete).
+__device__ __forceinline__ void seg_stage(const SegFetch &f, const uint32_t *starts, uint32_t pwr, uint32_t *slots,
+                                          uint32_t tid) {
 #pragma unroll
-    for (uint32_t k = 0; k < kPrefetch; ++k) prefetch_quad(pf, k, payload, lo, q_last, tid);
+    for (uint32_t k = 0; k < kSegQuads; ++k) {
+        const uint32_t seg = seg_of(k, tid), p4 = 4 * part_of(k, tid);
+        const uint32_t s = starts[seg];
+        // p4 unless the load was clamped (a start within the last words of
+        // the payload only occurs in a corrupt container: its words then
+        // land anywhere inside the segment)
+        const uint32_t d = min(min(s + p4, pwr - 4) - s, kSlotData - 4);
+        uint32_t *dst = slots + seg * kSlotWords + d;
+        dst[0] = f.q[k].x;
+        dst[1] = f.q[k].y;
+        dst[2] = f.q[k].z;
+        dst[3] = f.q[k].w;
+    }
 }
 
 // Tables into LDS (shared by both kernels).
 template <int MODE>
 __device__ __forceinline__ void load_tables(const uint8_t *cbb, uint4 *tab4, uint32_t tid) {
     if (MODE == kDecodeLut12) {
-        // 32-bit entries (18 - length) | symbol << 8 (0: no codeword)
+        // 16-bit entries (19 - length) | symbol << 8 (0: no codeword)
         const uint8_t *ds = cbb + kOffDecSym, *dl = cbb + kOffDecSym + 4096;
-        uint32_t *lut = reinterpret_cast<uint32_t *>(tab4);
+        uint16_t *lut = reinterpret_cast<uint16_t *>(tab4);
         for (uint32_t i = tid; i < 4096; i += kThreads) {
             const uint32_t len = dl[i];
-            lut[i] = len ? ((18 - len) | ((uint32_t)ds[i] << 8)) : 0u;
+            lut[i] = (uint16_t)(len ? ((kLutOff - len) | ((uint32_t)ds[i] << 8)) : 0u);
         }
     } else {
         // symbol of rank r, then zeros up to rank 1023 (a rank is below
@@ -532,11 +609,6 @@ __device__ __forceinline__ void qlc_area_regs(const uint8_t *cbb, Tables &t) {
     t.st_hi = st[1];
 }
 
-__device__ __forceinline__ bool span_staged(uint64_t lo, uint64_t hi, uint64_t payload_words, uint32_t stage_cap) {
-    const uint64_t wb = lo & ~(uint64_t)(kRow - 1);
-    return hi - wb <= stage_cap && payload_words > wb;
-}
-
 // Per-lane checks of a sub-stream against its group's span [wbase, hi).
 struct LaneJob {
     bool ok;
@@ -564,118 +636,209 @@ __device__ __forceinline__ LaneJob lane_job(LaneMeta m, bool kind_ok, uint64_t p
     return j;
 }
 
+// A lane's two segments, as start words relative to the group's base word:
+// a holds the sub-stream's first bit (the first half is decoded from words
+// a .. a + 39), b = max(e - 39, a) with e the word of its last bit (the
+// second half from b .. b + 39).  Rejected lanes use 0.
+struct SegJob {
+    LaneJob j;
+    uint32_t a, b;
+};
+
+__device__ __forceinline__ SegJob seg_job(const LaneMeta &m, bool kind_ok, uint64_t payload_words, uint64_t wbase,
+                                          uint64_t hi, uint32_t *status) {
+    SegJob s;
+    s.j = lane_job(m, kind_ok, payload_words, wbase, hi, status);
+    s.a = s.j.pos0 >> 5;
+    const uint32_t e = s.j.pos_want > 0 ? (s.j.pos_want - 1) >> 5 : 0;
+    s.b = max(e >= kSlotData - 1 ? e - (kSlotData - 1) : 0u, s.a);
+    return s;
+}
+
+// The base word of a group's relative indices (its first word, moved back so
+// that 4 words follow it: the kernel runs only when the payload has 4), and
+// the words from there to the end of the payload (capped at 2^28, so that
+// byte offsets fit 32 bits; relative indices of accepted lanes stay below
+// 2^26).
+__device__ __forceinline__ uint64_t group_base(uint64_t lo, uint64_t payload_words) {
+    return lo < payload_words - 4 ? lo : payload_words - 4;
+}
+
+__device__ __forceinline__ uint32_t words_left(uint64_t wbase, uint64_t payload_words) {
+    const uint64_t r = payload_words - wbase;
+    return (uint32_t)(r < (1ull << 28) ? r : (1ull << 28));
+}
+
+// One group from global memory (the leftover groups, and a group whose
+// halves do not fit their segments): each lane reads its words straight
+// from the payload and writes only bytes below its symbol count.
+template <int MODE>
+__device__ __forceinline__ void decode_group_global(uint64_t grp, const Tables &t, bool kind_ok,
+                                                    const uint32_t *payload, uint64_t payload_words,
+                                                    const uint32_t *chunk_bits, const uint64_t *cwo,
+                                                    const uint32_t *sub_off, uint64_t n, uint32_t chunk,
+                                                    uint64_t num_sub, uint64_t num_chunks, uint8_t *out,
+                                                    uint32_t *status, uint32_t tid) {
+    uint64_t lo, hi;
+    span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
+    const uint64_t wbase = lo;
+    const LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
+    const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
+    if (payload_words <= wbase) return;  // nothing readable: every lane was flagged
+    uint8_t *dst = out + (grp * kThreads + tid) * kSub;
+    GlobalWords src{payload + wbase, payload_words - wbase - 1};
+    uint32_t bad = no_invalid_yet<MODE>();
+    const uint32_t pos_end = decode_masked<MODE>(src, job.pos0, job.lim, t, dst, bad, 0, kSub);
+    if (job.ok && (saw_invalid<MODE>(bad, t) || pos_end != job.pos_want)) flag_corrupt(status);
+}
+
 // The group loop of a workgroup (CHECK: test every table entry for "no
-// codeword", needed only when the code is incomplete).  Every lane decodes
-// on every pass; a group whose span is not staged decodes stale rows and
-// stores nothing (it is decoded later as a leftover).
+// codeword", needed only when the code is incomplete).  Per group:
+//   B1  the segment area is free; the first-half segments (loaded during
+//       the previous group's second half) are written into it;
+//   B2  first half decoded; its steps issue the loads of the second-half
+//       segments; the next group's entries are loaded;
+//   B3  every lane checks that its first half ended inside its first
+//       segment and starts inside its second; the second-half segments are
+//       written into the segment area;
+//   B4  second half decoded; its steps issue the loads of the next group's
+//       first-half segments;
+//   B5  the output goes out through the segment area.
+// A group where any lane's half does not fit its segment (more than ~9.8
+// bits per symbol over 128 symbols) is decoded again from global memory, and
+// nothing of the staged pass is stored.
 template <int MODE, bool CHECK>
 __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const Tables &t, bool kind_ok,
-                                              uint32_t *stage, uint4 *stage4, const uint32_t *payload,
-                                              uint64_t payload_words, const uint32_t *chunk_bits,
-                                              const uint64_t *cwo, const uint32_t *sub_off, uint64_t n,
-                                              uint32_t chunk, uint64_t num_sub, uint64_t num_full,
-                                              uint64_t num_chunks, uint8_t *out, uint32_t *status,
-                                              uint32_t stage_cap) {
-    gquad *pq = opaque_quads(payload);
-    // ---- prologue: loads of the first group --------------------------
+                                              uint8_t *lds, const uint32_t *payload, uint64_t payload_words,
+                                              const uint32_t *chunk_bits, const uint64_t *cwo,
+                                              const uint32_t *sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub,
+                                              uint64_t num_full, uint64_t num_chunks, uint8_t *out,
+                                              uint32_t *status) {
+    uint32_t *starts_a = reinterpret_cast<uint32_t *>(lds + kOffStartsA);  // first halves, one group ahead
+    uint32_t *starts_b = reinterpret_cast<uint32_t *>(lds + kOffStartsB);  // second halves of this group
+    uint32_t *flag = reinterpret_cast<uint32_t *>(lds + kOffFlag);
+    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + kOffSlots);
+    gword *gp = opaque_words(payload);
+    // ---- prologue: the first group's entries and first-half segments ------
     LaneMeta meta = load_meta(grp * kThreads + tid0, num_sub, n, chunk, chunk_bits, cwo, sub_off);
     uint64_t lo, hi;
     span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
-    Prefetch pf;
-    issue_prefetch(pf, pq, lo, last_quad(lo, hi, payload_words), tid0);
+    uint64_t wbase = group_base(lo, payload_words);
+    SegJob sj = seg_job(meta, kind_ok, payload_words, wbase, hi, status);
     // the next group's span entries, one group ahead
     SpanEntries nspan = load_span(grp + gridDim.x < num_full ? grp + gridDim.x : grp, num_sub, chunk, num_chunks,
                                   cwo, sub_off);
+    starts_a[tid0] = sj.a;
+    if (tid0 == 0) *flag = 0;
+    __syncthreads();
+    SegFetch pf;
+    {
+        gword *gb = gp + wbase;
+        const uint32_t pwr = words_left(wbase, payload_words);
+#pragma unroll
+        for (uint32_t k = 0; k < kSetLoads; ++k)
+            seg_fetch(pf, k, starts_a[seg_of(k, tid0)], gb, pwr, tid0);
+    }
     uint32_t o1[kHalfWords], o2[kHalfWords];
 
     for (;;) {
         // the lane index as an opaque value: computations from it are not
         // hoisted out of the loop to hold dozens of registers across it
         const uint32_t tid = vgpr_copy(tid0);
-        const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
-        const uint64_t cnt = hi - wbase;
-        const bool staged = span_staged(lo, hi, payload_words, stage_cap);
-        // ---- stage the current group (its loads were issued earlier) --
-        __syncthreads();  // every lane is done with the previous group's rows
-        // wait for the whole prefetch here, on every path (waits left to the
-        // compiler would sit in the branches below, and every later write
-        // of these registers would wait again, for whatever is in flight)
+        gword *gb = gp + wbase;
+        const uint32_t pwr = words_left(wbase, payload_words);
+        starts_b[tid] = sj.b;
+        __syncthreads();  // B1
+        // wait for every load of the set here (waits left to the compiler
+        // would sit at each use, and every later write of these registers
+        // would wait again, for whatever is in flight)
 #pragma unroll
-        for (uint32_t k = 0; k < kPrefetch; ++k) {
+        for (uint32_t k = 0; k < kSegQuads; ++k) {
             pin(pf.q[k].x);
             pin(pf.q[k].y);
             pin(pf.q[k].z);
             pin(pf.q[k].w);
         }
-        if (staged) {
-            const uint32_t nq = (uint32_t)((cnt + 3) / 4);
-            const uint64_t full_q = (payload_words - wbase) / 4;
-#pragma unroll
-            for (uint32_t k = 0; k < kPrefetch; ++k) {
-                const uint32_t q = tid + k * kThreads;
-                if (q < nq && q < full_q) stage4[q] = pf.q[k];
-            }
-            if (nq > full_q && tid == (uint32_t)full_q % kThreads) {
-                // the span reaches the payload's last quad, which may be
-                // partial: its words are read one by one
-                uint32_t v[4];
-#pragma unroll
-                for (uint32_t w = 0; w < 4; ++w) {
-                    const uint64_t i = wbase + 4 * full_q + w;
-                    v[w] = i < payload_words ? payload[i] : 0u;
-                }
-                stage4[full_q] = make_uint4(v[0], v[1], v[2], v[3]);
-            }
-        }
-        __syncthreads();
+        seg_stage(pf, starts_a, pwr, slots, tid);
+        __syncthreads();  // B2
 
-        // ---- the next group's entries and payload ----------------------
-        // Loads and prefetch are issued on every pass (for the last, of this
-        // group's own entries and span again): control flow around them
-        // makes the compiler's wait counting conservative, and it then waits
-        // for the prefetch right after issuing it.
+        // ---- the next group's entries ---------------------------------
+        // loaded on every pass (for the last, this group's own again):
+        // control flow around loads makes the compiler's wait counting
+        // conservative
         const uint64_t nxt = grp + gridDim.x;
         const bool more = nxt < num_full;
         const uint64_t nxt_c = more ? nxt : grp;
         const LaneMeta nmeta = load_meta(nxt_c * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
         const uint64_t nn = nxt + gridDim.x;
         const SpanEntries nspan2 = load_span(nn < num_full ? nn : nxt_c, num_sub, chunk, num_chunks, cwo, sub_off);
-        uint64_t nlo = 0, nhi = 0, nq_lo = 0, nq_last = 0;
+        uint64_t nlo, nhi;
         span_words(nspan, payload_words, nlo, nhi);
-        nq_last = more ? last_quad(nlo, nhi, payload_words) : 0;
-        nq_lo = more ? nlo : 0;
-        const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
-        const LdsWords src{stage, (uint32_t)((cnt < stage_cap ? cnt : stage_cap) - (cnt > 0 ? 1 : 0))};
+        const LdsWords src{slots + tid * kSlotWords, kSlotData - 1};
         uint32_t bad = no_invalid_yet<MODE>();
-        // first half: the next group's payload loads, one per step (spread
-        // thinner than two per step over half the steps: measured faster);
-        // its span entries were loaded one group ahead
-        uint32_t pos = decode_half<MODE, CHECK>(src, job.pos0, t, bad, o1, [&](uint32_t q) {
-            prefetch_quad(pf, q, pq, nq_lo, nq_last, tid);
+
+        // ---- first half; its steps load the second-half segments --------
+        uint32_t st = starts_b[seg_of(0, tid)];
+        uint32_t pos = decode_half<MODE, CHECK>(src, sj.j.pos0 & 31, t, bad, o1, [&](uint32_t q) {
+            if (q < kSetLoads) {
+                seg_fetch(pf, q, st, gb, pwr, tid);
+                if (q + 1 < kSegQuads) st = starts_b[seg_of(q + 1, tid)];
+            }
         });
-        pos = decode_half<MODE, CHECK>(src, pos, t, bad, o2, [&](uint32_t) {});
-        if (staged && job.ok && (saw_invalid<MODE>(bad, t) || pos != job.pos_want)) flag_corrupt(status);
-        // the staging rows take the output once every lane is done with them
-        __syncthreads();
-        if (staged) store_group(stage4, out + grp * kThreads * kSub, tid, o1, o2);
+        // bits from the base word a to the end of the first half; the half
+        // must have ended inside segment a, and segment b must hold it
+        const uint32_t m = sj.a * 32 + pos;
+        const bool fail = sj.j.ok && (pos > kSlotBits || m < sj.b * 32);
+        const uint32_t pos2 = fail ? 0u : m - sj.b * 32;
+        // the next group's lane checks and first-half starts
+        const uint64_t nwbase = group_base(nlo, payload_words);
+        const SegJob nsj = seg_job(nmeta, kind_ok, payload_words, nwbase, nhi, status);
+        starts_a[tid] = nsj.a;
+        if (fail) atomicOr(flag, 1u);
+        __syncthreads();  // B3
+        const bool gfail = *flag != 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kSegQuads; ++k) {
+            pin(pf.q[k].x);
+            pin(pf.q[k].y);
+            pin(pf.q[k].z);
+            pin(pf.q[k].w);
+        }
+        seg_stage(pf, starts_b, pwr, slots, tid);
+        __syncthreads();  // B4
+        if (tid == 0) *flag = 0;
+
+        // ---- second half; its steps load the next group's first halves --
+        gword *ngb = gp + nwbase;
+        const uint32_t npwr = words_left(nwbase, payload_words);
+        st = starts_a[seg_of(0, tid)];
+        pos = decode_half<MODE, CHECK>(src, pos2, t, bad, o2, [&](uint32_t q) {
+            if (q < kSetLoads) {
+                seg_fetch(pf, q, st, ngb, npwr, tid);
+                if (q + 1 < kSegQuads) st = starts_a[seg_of(q + 1, tid)];
+            }
+        });
+        if (!gfail && sj.j.ok && (saw_invalid<MODE>(bad, t) || pos != sj.j.pos_want - sj.b * 32))
+            flag_corrupt(status);
+        __syncthreads();  // B5: the slots take the output
+        if (!gfail)
+            store_group(reinterpret_cast<uint4 *>(slots), out + grp * kThreads * kSub, tid, o1, o2);
+        else
+            decode_group_global<MODE>(grp, t, kind_ok, payload, payload_words, chunk_bits, cwo, sub_off, n, chunk,
+                                      num_sub, num_chunks, out, status, tid);
 
         if (!more) break;
         grp = nxt;
-        meta = nmeta;
-        lo = nlo;
-        hi = nhi;
+        wbase = nwbase;
+        sj = nsj;
         nspan = nspan2;
     }
 }
 
-// The groups the main kernel leaves: those whose span exceeds the LDS
-// budget (the same span test picks them) and the last group when it is not
-// full.  Each lane reads its words straight from global memory and writes
-// only bytes below its symbol count.  Workgroup b owns the groups b, b + G,
-// b + 2G, ... (G workgroups); its first wave tests 64 of them at once (one
-// per lane), then the workgroup decodes the ones that were not staged, so
-// that a stream with no such group costs one round of entry loads, and a
-// stream of such groups is spread over all workgroups.
+// The groups the main kernel leaves: the last group when it is not full
+// (decoded from global memory, see decode_group_global).  Workgroup b owns
+// the groups b, b + G, b + 2G, ... (G workgroups); its first wave tests 64
+// of them at once (one per lane).
 constexpr uint32_t kTestBatch = 64;
 
 struct Leftovers {
@@ -686,16 +849,12 @@ struct Leftovers {
 // Test the batch of groups base + l G, l = 0 .. 63: the ones for the
 // global-memory path go to lo.todo; returns their number (uniform).
 __device__ __forceinline__ uint32_t test_batch(Leftovers &lo_, uint64_t base, uint64_t G, uint64_t num_groups,
-                                               uint64_t num_full, uint64_t num_sub, uint32_t chunk,
-                                               uint64_t num_chunks, const uint64_t *cwo, const uint32_t *sub_off,
-                                               uint64_t payload_words, uint32_t stage_cap, uint32_t tid) {
+                                               uint64_t num_full, uint32_t tid) {
     if (tid == 0) lo_.ntodo = 0;
     __syncthreads();
     if (tid < kTestBatch && base + tid * G < num_groups) {
         const uint64_t g = base + tid * G;
-        uint64_t lo, hi;
-        span_words_lane(load_span(g, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
-        if (g >= num_full || !span_staged(lo, hi, payload_words, stage_cap)) lo_.todo[atomicAdd(&lo_.ntodo, 1u)] = tid;
+        if (g >= num_full) lo_.todo[atomicAdd(&lo_.ntodo, 1u)] = tid;
     }
     __syncthreads();
     return uniform(lo_.ntodo);
@@ -709,73 +868,57 @@ __device__ __forceinline__ void decode_batch(const Leftovers &lo_, uint32_t nt, 
                                              const uint64_t *cwo, const uint32_t *sub_off, uint64_t n,
                                              uint32_t chunk, uint64_t num_sub, uint64_t num_chunks, uint8_t *out,
                                              uint32_t *status, uint32_t tid) {
-    for (uint32_t i = 0; i < nt; ++i) {
-        const uint64_t grp = base + lo_.todo[i] * G;
-        uint64_t lo, hi;
-        span_words(load_span(grp, num_sub, chunk, num_chunks, cwo, sub_off), payload_words, lo, hi);
-        const uint64_t wbase = lo & ~(uint64_t)(kRow - 1);
-        const LaneMeta meta = load_meta(grp * kThreads + tid, num_sub, n, chunk, chunk_bits, cwo, sub_off);
-        const LaneJob job = lane_job(meta, kind_ok, payload_words, wbase, hi, status);
-        if (payload_words <= wbase) continue;  // nothing readable: every lane was flagged
-        uint8_t *dst = out + (grp * kThreads + tid) * kSub;
-        GlobalWords src{payload + wbase, payload_words - wbase - 1};
-        uint32_t bad = no_invalid_yet<MODE>();
-        const uint32_t pos_end = decode_masked<MODE>(src, job.pos0, job.lim, t, dst, bad, 0, kSub);
-        if (job.ok && (saw_invalid<MODE>(bad, t) || pos_end != job.pos_want)) flag_corrupt(status);
-    }
+    for (uint32_t i = 0; i < nt; ++i)
+        decode_group_global<MODE>(base + lo_.todo[i] * G, t, kind_ok, payload, payload_words, chunk_bits, cwo,
+                                  sub_off, n, chunk, num_sub, num_chunks, out, status, tid);
 }
 
 // Main kernel: the full groups (all 256 sub-streams of 256 symbols inside
-// [0, n)) whose span fits the staging rows, so no lane needs masking, then
-// the workgroup's leftover groups.  Each
-// half's 128 bytes per lane are stored as soon as they are decoded.  Lanes
-// of a corrupt sub-stream decode from the start of the staged span (LDS
+// [0, n)), so no lane needs masking, then the workgroup's leftover groups.
+// Lanes of a corrupt sub-stream decode from somewhere in their segments (LDS
 // reads are clamped) and write unspecified bytes into their own 256-byte
-// range.
+// range.  Three workgroups share a CU (LDS: the table and two segments of 33
+// words per lane; at most 168 VGPRs).
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void decode_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(
     const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
     const uint32_t *__restrict__ chunk_bits, const uint64_t *__restrict__ cwo,
     const uint32_t *__restrict__ sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub, uint64_t num_full,
-    uint64_t num_chunks, uint64_t num_groups, uint8_t *__restrict__ out, uint32_t *__restrict__ status,
-    uint32_t stage_cap) {
-    // Tables at fixed LDS addresses (folded into the instructions' offset
-    // fields); the payload staging rows are the dynamic part.
-    __shared__ uint4 tab4[MODE == kDecodeLut12 ? kLutBytes / 16 : 64];
-    __shared__ Leftovers left;
-    extern __shared__ uint4 stage4[];
-    uint32_t *stage = reinterpret_cast<uint32_t *>(stage4);
+    uint64_t num_chunks, uint64_t num_groups, uint8_t *__restrict__ out, uint32_t *__restrict__ status) {
+    // everything at fixed LDS addresses (folded into the instructions'
+    // offset fields)
+    __shared__ uint4 lds4[kLdsBytes / 16];
+    uint8_t *lds = reinterpret_cast<uint8_t *>(lds4);
+    Leftovers &left = *reinterpret_cast<Leftovers *>(lds + kOffLeft);
     const uint32_t tid = threadIdx.x;
     const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
     const pc_codebook *cbp = reinterpret_cast<const pc_codebook *>(cb);
-    load_tables<MODE>(cbb, tab4, tid);
+    load_tables<MODE>(cbb, lds4, tid);
     const bool kind_ok = MODE == kDecodeLut12 || cbp->kind == PC_CODEBOOK_QLC;
     Tables t;
-    t.lut = reinterpret_cast<const uint32_t *>(tab4);
-    t.sym = reinterpret_cast<const uint8_t *>(tab4);
+    t.lut = reinterpret_cast<const uint32_t *>(lds4);
+    t.sym = reinterpret_cast<const uint8_t *>(lds4);
     if (MODE == kDecodeQlc) qlc_area_regs(cbb, t);
 
-    // this workgroup's first batch of leftover groups (see below), tested
-    // while the tables arrive; decoded after the staged groups
+    // this workgroup's first batch of leftover groups, tested while the
+    // tables arrive; decoded after the full groups
     const uint64_t G = gridDim.x;
-    const uint32_t nt0 = test_batch(left, blockIdx.x, G, num_groups, num_full, num_sub, chunk, num_chunks, cwo,
-                                    sub_off, payload_words, stage_cap, tid);
+    const uint32_t nt0 = test_batch(left, blockIdx.x, G, num_groups, num_full, tid);
     const uint64_t grp = blockIdx.x;
     if (grp < num_full) {
         if (cbp->complete == 1)
-            decode_groups<MODE, false>(grp, tid, t, kind_ok, stage, stage4, payload, payload_words, chunk_bits, cwo,
-                                       sub_off, n, chunk, num_sub, num_full, num_chunks, out, status, stage_cap);
+            decode_groups<MODE, false>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo, sub_off,
+                                       n, chunk, num_sub, num_full, num_chunks, out, status);
         else
-            decode_groups<MODE, true>(grp, tid, t, kind_ok, stage, stage4, payload, payload_words, chunk_bits, cwo,
-                                      sub_off, n, chunk, num_sub, num_full, num_chunks, out, status, stage_cap);
+            decode_groups<MODE, true>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo, sub_off, n,
+                                      chunk, num_sub, num_full, num_chunks, out, status);
     }
     __syncthreads();  // the tables are in LDS
     decode_batch<MODE>(left, nt0, blockIdx.x, G, t, kind_ok, payload, payload_words, chunk_bits, cwo, sub_off, n,
                        chunk, num_sub, num_chunks, out, status, tid);
     for (uint64_t base = blockIdx.x + G * kTestBatch; base < num_groups; base += G * kTestBatch) {
         __syncthreads();  // the previous batch's list is read
-        const uint32_t nt = test_batch(left, base, G, num_groups, num_full, num_sub, chunk, num_chunks, cwo, sub_off,
-                                       payload_words, stage_cap, tid);
+        const uint32_t nt = test_batch(left, base, G, num_groups, num_full, tid);
         decode_batch<MODE>(left, nt, base, G, t, kind_ok, payload, payload_words, chunk_bits, cwo, sub_off, n, chunk,
                            num_sub, num_chunks, out, status, tid);
     }
@@ -787,8 +930,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
     const uint32_t *__restrict__ chunk_bits, const uint64_t *__restrict__ cwo,
     const uint32_t *__restrict__ sub_off, uint64_t n, uint32_t chunk, uint64_t num_sub, uint64_t num_groups,
-    uint64_t num_full, uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status,
-    uint32_t stage_cap) {
+    uint64_t num_full, uint64_t num_chunks, uint8_t *__restrict__ out, uint32_t *__restrict__ status) {
     __shared__ uint4 tab4[MODE == kDecodeLut12 ? kLutBytes / 16 : 64];
     __shared__ Leftovers left;
     const uint32_t tid = threadIdx.x;
@@ -802,8 +944,7 @@ __global__ __launch_bounds__(kThreads) void decode_global_kernel(
     if (MODE == kDecodeQlc) qlc_area_regs(cbb, t);
     const uint64_t G = gridDim.x;
     for (uint64_t base = blockIdx.x; base < num_groups; base += G * kTestBatch) {
-        const uint32_t nt = test_batch(left, base, G, num_groups, num_full, num_sub, chunk, num_chunks, cwo, sub_off,
-                                       payload_words, stage_cap, tid);
+        const uint32_t nt = test_batch(left, base, G, num_groups, num_full, tid);
         if (nt && !loaded) {
             load_tables<MODE>(cbb, tab4, tid);
             __syncthreads();
@@ -825,16 +966,10 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     const uint64_t last = n - (nc - 1) * chunk;
     const uint64_t num_sub = (nc - 1) * (chunk / kSub) + (last + kSub - 1) / kSub;
     const uint64_t num_groups = (num_sub + kThreads - 1) / kThreads;
-    // LDS budget for a staged span: two workgroups share a CU's 160 KiB:
-    // kStageWords words (+ 4 spare) beside the 8 KiB of tables.
-    const uint64_t cap = kStageWords;
-    const size_t shmem = kStageBytes;
-    // Per device (the current one), set once: its CU count, and the
-    // dynamic-LDS limit of the main kernels.  Concurrent first calls may
-    // both query and set; they store the same values.
+    // Per device (the current one), its CU count, queried once.  Concurrent
+    // first calls may both query; they store the same value.
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cus_of[kMaxDevices];
-    static std::atomic<bool> attr_of[kMaxDevices][2];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -845,15 +980,8 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
         if (e != hipSuccess) return e;
         cus_of[dev].store(num_cus, std::memory_order_relaxed);
     }
-    const void *fn = mode == kDecodeLut12 ? (const void *)decode_kernel<kDecodeLut12>
-                                          : (const void *)decode_kernel<kDecodeQlc>;
-    if (!attr_of[dev][mode].load(std::memory_order_relaxed)) {
-        e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kStageBytes);
-        if (e != hipSuccess) return e;
-        attr_of[dev][mode].store(true, std::memory_order_relaxed);
-    }
     // groups whose 256 sub-streams all hold 256 symbols inside [0, n)
-    // (the main kernel's prefetch needs one whole 16-byte quad of payload)
+    // (the main kernel's segment loads need four words of payload)
     const uint64_t num_full = payload_words >= 4 ? n / ((uint64_t)kThreads * kSub) : 0;
     uint64_t grid = (uint64_t)num_cus * kGroupsPerCU;
     if (grid > num_full) grid = num_full;
@@ -861,13 +989,11 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     if (grid_g > num_groups) grid_g = num_groups;
     if (num_sub >= kMaxDecodeSubstreams) return hipErrorInvalidValue;  // the entry point checks first
 #define PC_DEC(K)                                                                                             \
-    hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), shmem, stream, cb, payload, payload_words,     \
-                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_full, nc, num_groups, out, status,    \
-                       (uint32_t)cap)
+    hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), 0, stream, cb, payload, payload_words,         \
+                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_full, nc, num_groups, out, status)
 #define PC_DEC_G(K)                                                                                           \
     hipLaunchKernelGGL(K, dim3((uint32_t)grid_g), dim3(kThreads), 0, stream, cb, payload, payload_words,       \
-                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, num_full, nc, out, status,    \
-                       (uint32_t)cap)
+                       chunk_bits, cwo, sub_off, n, chunk, num_sub, num_groups, num_full, nc, out, status)
     // with a full group the main kernel also takes the leftover groups;
     // without one, only the leftover kernel runs
     if (mode == kDecodeLut12) {

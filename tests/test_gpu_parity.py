@@ -234,8 +234,8 @@ def test_group_boundaries():
 
 
 def light(n, seed):
-    """e4m3 of N(0,1): about 6.5 bits per symbol under a code built for it,
-    light enough for the 320-lane decode geometry."""
+    """e4m3 of N(0,1): about 6.5 bits per symbol under a code built for it
+    (the density of the 1 GiB benchmark stream)."""
     rng = np.random.default_rng(seed)
     return W.e4m3_from_f32(rng.standard_normal(max(n, 1), dtype=np.float32))[:n]
 
@@ -245,9 +245,9 @@ def light_book(kind="huffman", bits=None):
 
 
 def test_light_group_boundaries():
-    """Streams of about 6.5 bits per symbol take the 320-lane geometry (groups
-    of 320 sub-streams, 81920 symbols) once there is a full group: sizes around
-    whole groups, around the smaller 256-lane groups, and ragged ends."""
+    """Streams of about 6.5 bits per symbol at sizes off the 65536-symbol
+    group grid (steps of 81920 symbols, ragged ends): full groups decoded out
+    of the LDS segments, the ragged last group from global memory."""
     for kind, bits in (("huffman", None), ("qlc", (1, 3, 3, 3, 3, 5, 6, 7))):
         dcb, obook = light_book(kind, bits)
         for chunk in (4096, 65536):
@@ -260,22 +260,22 @@ def test_light_group_boundaries():
                     assert int(host(enc)["chunk_bits"].astype(np.int64).sum()) < 6.9 * n
 
 
-def test_density_gate_both_sides():
+def test_dense_and_light_segments():
     """Segments of 81920 symbols, light data with every k-th segment uniform
-    random bytes (about 11 bits per symbol under the light code): one in 40
-    keeps the stream below the 6.9 bits per symbol gate (320-lane geometry,
-    its dense groups decoded as leftovers), one in 6 puts it above (256-lane
-    geometry, dense groups again leftovers)."""
+    random bytes (about 11 bits per symbol under the light code, so their
+    halves overflow the 40-word LDS segments and their groups are decoded
+    again from global memory): one in 40 and one in 6 such segments, i.e. a
+    stream below and one above 6.9 bits per symbol on average."""
     dcb, obook = light_book()
     rng = np.random.default_rng(5)
     for every, want_light in ((40, True), (6, False)):
         segs = [rng.integers(0, 256, 81920, dtype=np.uint8) if i % every == every - 1 else light(81920, 500 + i)
                 for i in range(90)]
         x_np = np.concatenate(segs + [light(999, 3)])
-        say("density gate: dense segment every", every)
+        say("dense and light segments: dense segment every", every)
         enc = roundtrip(dcb, obook, x_np, 16384)
         bps = host(enc)["chunk_bits"].astype(np.int64).sum() / x_np.size
-        say("density gate: %.3f bits per symbol" % bps)
+        say("dense and light segments: %.3f bits per symbol" % bps)
         assert (bps <= 6.9) == want_light
 
 
@@ -316,9 +316,10 @@ def test_degenerate_data(kind):
         "one_rare_symbol": np.full(100_000, int(np.argmax(lengths)), np.uint8),
         "uniform": np.tile(np.arange(256, dtype=np.uint8), 400),
         "unseen_symbols_only": np.arange(40, 256, dtype=np.uint8).repeat(300),
-        # whole groups of 65536 symbols: a compressible one (staged in LDS),
-        # two of 12-bit codewords (too large to stage), a ragged tail
-        "staged_and_unstaged_groups": np.concatenate([
+        # whole groups of 65536 symbols: a compressible one (decoded out of
+        # the LDS segments), two of 12-bit codewords (halves too long for a
+        # segment: decoded from global memory), a ragged tail
+        "segment_and_global_groups": np.concatenate([
             np.tile(np.arange(40, dtype=np.uint8), 1639)[:65536],
             np.tile(np.arange(40, 256, dtype=np.uint8), 607)[:131072],
             np.arange(40, dtype=np.uint8).repeat(25)]),
@@ -331,9 +332,9 @@ def test_degenerate_data(kind):
 @pytest.mark.parametrize("chunk", [4096, 8192, 16384, 32768, 65536])
 def test_incompressible_data(chunk):
     """Uniform random bytes under the code of their own (flat) histogram: 8
-    bits per symbol, the most a staged group may hold (a group's span is
-    16384 words), and with one byte value made rarer, 8+ bits for some
-    groups (decoded from global memory)."""
+    bits per symbol (a half of 128 symbols takes 32 of a segment's 40
+    words), and with two byte values made rarer, 9-bit codes for some
+    symbols."""
     rng = np.random.default_rng(77)
     n = 3 * 65536 + 1000
     x_np = rng.integers(0, 256, n, dtype=np.uint8)
@@ -350,12 +351,13 @@ def test_incompressible_data(chunk):
 
 
 
-def test_staged_and_leftover_groups_mixed():
-    """Many groups, every third one too large to stage: segments of 65536
-    bytes alternate between data the code fits and uniform random bytes it
-    codes at more than 8 bits per symbol.  Workgroups then meet unstaged
-    groups in the middle of their persistent loop and decode them, with the
-    ragged last group, after their staged ones."""
+def test_segment_and_global_groups_mixed():
+    """Many groups, every third one too dense for the LDS segments: segments
+    of 65536 bytes alternate between data the code fits and uniform random
+    bytes it codes at more than 8 bits per symbol.  Workgroups then meet
+    groups whose halves do not fit in the middle of their persistent loop
+    and decode them again from global memory; the ragged last group comes
+    after their full groups."""
     counts = np.bincount(skewed(1 << 20, 41), minlength=256).astype(np.int64)
     dcb, obook = make_book(counts, "huffman", None)
     rng = np.random.default_rng(43)
@@ -363,7 +365,7 @@ def test_staged_and_leftover_groups_mixed():
     for i in range(1100):
         segs.append(rng.integers(0, 256, 65536, dtype=np.uint8) if i % 3 == 2 else skewed(65536, 1000 + i))
     x_np = np.concatenate(segs + [skewed(777, 7)])
-    say("staged and leftover groups: n", x_np.size)
+    say("segment and global groups: n", x_np.size)
     enc = roundtrip(dcb, obook, x_np, 65536)
     bits = host(enc)["chunk_bits"].astype(np.int64)
     assert (bits[2:1100:3] > 8 * 65536).all() and (bits[0:1100:3] < 8 * 65536).all()
