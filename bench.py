@@ -92,9 +92,9 @@ def pmc_summary(fetch_dir, write_dir, copy_bytes, out=TRAFFIC_FILE):
     lines = ["# HBM traffic per dispatch from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of bench.py.",
              "# Made by (from the repository root, after cd /tmp && export TMPDIR=/tmp):",
              "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d %s -o bench -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs" % fetch_dir,
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs --no-secondary" % fetch_dir,
              "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d %s -o bench -- "
-             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs" % write_dir,
+             "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs --no-secondary" % write_dir,
              "#   python3 bench.py --pmc-summary %s %s" % (fetch_dir, write_dir),
              "# Each counter is scaled by copy_bytes / counter(copy of copy_bytes bytes made with the coder",
              "# kernels' 16-byte non-temporal loads and stores, pc_traffic_probe); the scale from the runtime's",

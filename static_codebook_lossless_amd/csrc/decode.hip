@@ -74,8 +74,11 @@ static_assert(kThreads * kSlotWords * 4 >= 4 * 8192, "the output transpose fits 
 // 512 or 1280 bytes
 static_assert(3 * ((kLdsBytes + 1279) / 1280 * 1280) <= 160 * 1024, "three workgroups per CU");
 
+// First error wins.  The plain read first keeps a corrupt stream, where
+// every lane may report, from serialising millions of atomics on one word.
 __device__ __forceinline__ void flag_corrupt(uint32_t *status) {
-    atomicCAS(status, 0u, (uint32_t)PC_ERR_CORRUPT);
+    if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+        atomicCAS(status, 0u, (uint32_t)PC_ERR_CORRUPT);
 }
 
 // Payload word sources.  Indices are clamped so that corrupt positions never
@@ -209,20 +212,31 @@ __device__ __forceinline__ void lut16_step8(const Src &src, uint32_t &npos, uint
 }
 
 // The same decoder for a complete code (no "no codeword" entries) and all 8
-// symbols owed, with the window's word index q carried from step to step:
-// the next step's q is taken from the sum of the first 7 entries before the
-// 8th arrives, so the chain from the 8th entry to the next window read is a
-// subtract, a clamp, a shift and an address.  basem4 is the LDS byte address
-// of the lane's words minus 4 (the window starts at word q - 1).
+// symbols owed.  The next step's window word index is taken from the sum of
+// the first 7 entries before the 8th arrives, so the chain from the 8th entry
+// to the next window read is a subtract, a clamp, a shift and an address;
+// that read is issued before the 8 symbols are packed and before the step's
+// side work.  basem4 is the LDS byte address of the lane's words minus 4 (a
+// window starts at word q - 1).
 typedef const __attribute__((address_space(3))) uint32_t lds_u32;
 
-__device__ __forceinline__ void lut16_step8_fast(uint32_t basem4, uint32_t qlim, uint32_t &npos, uint32_t &q,
-                                                 const uint32_t *lut, uint32_t &o0, uint32_t &o1) {
+struct Win4 {
+    uint32_t w0, w1, w2, w3;
+};
+
+__device__ __forceinline__ Win4 read_win(uint32_t basem4, uint32_t q, uint32_t qlim) {
     lds_u32 *p = (lds_u32 *)(size_t)(basem4 + (min(q, qlim) << 2));
-    const uint32_t w0 = p[0], w1 = p[1], w2 = p[2], w3 = p[3];
-    uint32_t h = __builtin_amdgcn_alignbit(w0, w1, npos);
-    uint32_t m = __builtin_amdgcn_alignbit(w1, w2, npos);
-    uint32_t l = __builtin_amdgcn_alignbit(w2, w3, npos);
+    return Win4{p[0], p[1], p[2], p[3]};
+}
+
+// One step from the window words read a step earlier; when NEXT, it also
+// reads the next step's words.
+template <bool NEXT, class Side>
+__device__ __forceinline__ void lut16_step8_fast(Win4 &win, uint32_t basem4, uint32_t qlim, uint32_t &npos,
+                                                 const uint32_t *lut, uint32_t &o0, uint32_t &o1, Side &&side) {
+    uint32_t h = __builtin_amdgcn_alignbit(win.w0, win.w1, npos);
+    uint32_t m = __builtin_amdgcn_alignbit(win.w1, win.w2, npos);
+    uint32_t l = __builtin_amdgcn_alignbit(win.w2, win.w3, npos);
     uint32_t a = (h >> kLutOff) & kLutMask;
     const uint32_t K = 31u - npos + 8 * kLutOff;
     const uint8_t *lb = reinterpret_cast<const uint8_t *>(lut);
@@ -249,11 +263,15 @@ __device__ __forceinline__ void lut16_step8_fast(uint32_t basem4, uint32_t qlim,
         e[k] = ek;
     }
     // (31 - npos') / 32 for npos' = npos + sum(19 - length) - 8 * 19
-    q = (K6 - (e[7] & 0xFF)) >> 5;
+    if (NEXT) win = read_win(basem4, (K6 - (e[7] & 0xFF)) >> 5, qlim);
+    asm volatile("" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]), "+v"(e[6]),
+                 "+v"(e[7])::"memory");
     npos += ((T + e[7]) & 0xFF) - 8 * kLutOff;
     o0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) | __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
     o1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) | __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
     asm volatile("" : "+v"(o0), "+v"(o1));
+    side();
+    asm volatile("" ::: "memory");  // the side work stays at this step
 }
 
 // QLC decoder, 8 symbols from the 96-bit window (h, m, l); returns them
@@ -373,13 +391,12 @@ __device__ __forceinline__ uint32_t decode_half(const LdsWords &src, uint32_t po
     pos = to_step_pos<MODE>(pos);
     if (MODE == kDecodeLut12 && !CHECK) {
         const uint32_t basem4 = (uint32_t)(size_t)(lds_u32 *)src.w - 4u;
-        uint32_t wq = (31u - pos) >> 5;
+        Win4 win = read_win(basem4, (31u - pos) >> 5, src.last + 1);
 #pragma unroll
-        for (uint32_t q = 0; q < kHalf / 8; ++q) {
-            lut16_step8_fast(basem4, src.last + 1, pos, wq, t.lut, o[2 * q], o[2 * q + 1]);
-            side(q);
-            asm volatile("" ::: "memory");  // the side work stays at this step
-        }
+        for (uint32_t q = 0; q < kHalf / 8 - 1; ++q)
+            lut16_step8_fast<true>(win, basem4, src.last + 1, pos, t.lut, o[2 * q], o[2 * q + 1], [&] { side(q); });
+        constexpr uint32_t ql = kHalf / 8 - 1;
+        lut16_step8_fast<false>(win, basem4, src.last + 1, pos, t.lut, o[2 * ql], o[2 * ql + 1], [&] { side(ql); });
     } else {
 #pragma unroll
         for (uint32_t q = 0; q < kHalf / 8; ++q) {
