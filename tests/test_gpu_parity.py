@@ -233,6 +233,25 @@ def test_group_boundaries():
                 roundtrip(dcb, obook, skewed(n, n), chunk, qlc_decoder=(kind == "qlc"))
 
 
+def test_full_groups_tight_payload():
+    """Whole groups only, decoded with payload_words equal to the payload's
+    exact length: the last sub-streams' LDS segments reach past the end of
+    the payload, so their loads are clamped to its last four words and
+    written at their true positions; nothing outside [0, n) is written."""
+    for kind, bits in (("huffman", None), ("qlc", (1, 3, 3, 3, 3, 5, 6, 7))):
+        dcb, obook = make_book(random_counts(29), kind, bits)
+        for chunk in (4096, 65536):
+            for n in (65536, 3 * 65536):
+                x_np = skewed(n, n + chunk)
+                say("tight payload:", kind, "chunk", chunk, "n", n)
+                x, enc = gpu_encode(dcb, x_np, chunk)
+                total = int(enc.chunk_word_offset[-1].item())
+                for qlc in ((False, True) if kind == "qlc" else (False,)):
+                    out, st = decode_guarded(dcb, enc, total, qlc=qlc)
+                    assert st == 0
+                    assert torch.equal(out, x)
+
+
 def light(n, seed):
     """e4m3 of N(0,1): about 6.5 bits per symbol under a code built for it
     (the density of the 1 GiB benchmark stream)."""
