@@ -98,8 +98,9 @@ struct LdsWords {
     }
     __device__ __forceinline__ void fetch4m(uint32_t q, uint32_t (&v)[4]) const {
         // q = last + 1 is a lane whose remaining bits all lie in the last
-        // word (read as word q - 1); the spare words after the span keep the
-        // reads of q .. q + 2 inside the allocation
+        // word (read as word q - 1); the next segment, or the spare words
+        // after the last one, keep the reads of q .. q + 2 inside the
+        // allocation
         q = min(q, last + 1);
         const uint32_t *p = w + q - 1;
         v[0] = p[0];
