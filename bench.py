@@ -5,7 +5,10 @@ One step = the whole hot path over one batch: pc_encode (codeword lookup,
 bit-length scan, cross-chunk scan, bit packing, stores) followed by pc_decode
 (side-index sub-streams through the 12-bit peek table) of the same stream.
 Inputs are resident in HBM before timing starts; the codebook is built
-offline from previous batches and is not timed.
+offline from previous batches and is not timed.  Before the W warmup steps,
+untimed steps run until their time stops falling (the GPU's first ~25
+encode/decode pairs after start-up are up to 15-20% slower; the line reports
+the steady state and the number of such steps as `settle_steps`).
 
 Prints one JSON line.  `value` = uncompressed bytes per second of the round
 trip (n / step time), in GB/s.  Also reported: encode-only and decode-only
@@ -127,9 +130,11 @@ def _short_kernel(name):
     return n[:i] if i > 0 else n
 
 
-def trace_summary(trace_dir, out, command, title=None):
+def trace_summary(trace_dir, out, command, title=None, last=0):
     """Per-kernel lines (calls, average/min/max ns, share) from a
-    rocprofv3 --kernel-trace --stats --output-format csv run."""
+    rocprofv3 --kernel-trace --stats --output-format csv run; with ``last``,
+    also the coder kernels' mean over their last ``last`` dispatches (the
+    timed steps, after the settle and warmup steps)."""
     import csv
 
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
@@ -148,6 +153,20 @@ def trace_summary(trace_dir, out, command, title=None):
              "# Columns: calls, average ns, min ns, max ns, share of GPU time, kernel"]
     for c, avg, mn, mx, pct, name in rows[:12]:
         lines.append("%6d %10.0f %10.0f %10.0f %7.2f%%  %s" % (c, avg, mn, mx, pct, name[:90]))
+    if last:
+        tfiles = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+        durs = {}
+        with open(tfiles[0]) as f:
+            for r in csv.DictReader(f):
+                for kind, kname in KERNEL_NAMES.items():
+                    if kname in r["Kernel_Name"]:
+                        durs.setdefault(kind, []).append(
+                            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        lines.append("# Timed steps only (the last %d dispatches of each coder kernel): mean, min, max ns" % last)
+        for kind, d in sorted(durs.items()):
+            t = [v for _, v in sorted(d)[-last:]]
+            lines.append("%6d %10.0f %10.0f %10.0f           %s" % (len(t), sum(t) / len(t), min(t), max(t),
+                                                                 KERNEL_NAMES[kind]))
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -307,6 +326,32 @@ def _cpu_model():
 # ---------------------------------------------------------------------------
 
 
+def settle(fn, block=5, max_calls=80, tol=0.015):
+    """Untimed calls of fn (the work about to be timed), in blocks of
+    ``block``, until a block's mean time is no more than ``tol`` below the
+    previous block's (or ``max_calls`` calls); returns the number of calls.
+    On these GPUs the first ~25 encode/decode pairs after start-up, or after
+    an idle gap, run up to 15-20% slower than the ones after them, whatever
+    ran before (device copies and fp32 GEMMs as a first load do not remove
+    it); the timed calls are meant to see the steady state."""
+    import torch
+
+    prev, calls = None, 0
+    while calls < max_calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(block):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        calls += block
+        cur = e0.elapsed_time(e1) / block
+        if prev is not None and cur >= prev * (1.0 - tol):
+            break
+        prev = cur
+    return calls
+
+
 def time_calls(fn, reps):
     """Mean milliseconds of fn() (device work, timed with events on the
     current stream) over reps calls after two warmup calls."""
@@ -344,13 +389,16 @@ def qlc_leg(pc, W, dev):
     outs = pc.alloc_encode_outputs(n, w.chunk, dev)
     out = torch.empty(n, dtype=torch.uint8, device=dev)
     st = torch.zeros(1, dtype=torch.int32, device=dev)
+    settle(lambda: pc.pc_encode(dq, x, w.chunk, outs))
     enc_ms = time_calls(lambda: pc.pc_encode(dq, x, w.chunk, outs), 10)
     enc = pc.pc_encode(dq, x, w.chunk, outs)
     torch.cuda.synchronize()
     enc_ok = int(enc.status.item()) == 0
+    settle(lambda: pc.pc_decode(dq, enc, out=out, status=st))
     dec_ms = time_calls(lambda: pc.pc_decode(dq, enc, out=out, status=st), 10)
     ok_lut = int(st.item()) == 0 and bool(torch.equal(out, x))
     st.zero_()
+    settle(lambda: pc.pc_decode_qlc(dq, enc, out=out, status=st))
     qdec_ms = time_calls(lambda: pc.pc_decode_qlc(dq, enc, out=out, status=st), 10)
     ok_qlc = int(st.item()) == 0 and bool(torch.equal(out, x))
     xc = pc.pc_histogram(x).cpu().numpy().astype(np.float64)
@@ -415,6 +463,7 @@ def config_leg(pc, W, name, dev, reps, decoders):
     st = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def timed(fn):
+        settle(fn)
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -487,6 +536,8 @@ def main():
     ap.add_argument("--trace-command", default="")
     ap.add_argument("--trace-out", default="coder_kernels_stream_1g_kernel_trace.txt")
     ap.add_argument("--trace-title", default=None)
+    ap.add_argument("--trace-last", type=int, default=0,
+                    help="with --trace-summary: also the mean of each coder kernel's last N dispatches")
     ap.add_argument("--sq-summary", nargs="+", metavar="PMC_DIR")
     ap.add_argument("--sq-commands", nargs="*", default=[])
     ap.add_argument("--no-secondary", action="store_true",
@@ -499,7 +550,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.trace_summary:
         trace_summary(args.trace_summary, os.path.join(ROOT, "profiles", os.path.basename(args.trace_out)),
-                      args.trace_command, args.trace_title)
+                      args.trace_command, args.trace_title, args.trace_last)
         return 0
     if args.sq_summary:
         sq_summary(args.sq_summary, os.path.join(ROOT, "profiles", "coder_kernels_stream_1g_sq_counters.txt"),
@@ -553,6 +604,19 @@ def main():
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     decode = pc.pc_decode_qlc if args.decoder == "qlc" else pc.pc_decode
 
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        enc = pc.pc_encode(dcb, x, chunk, outs)
+        if evs:
+            evs[1].record()
+        decode(dcb, enc, out=dec_out, status=status)
+        if evs:
+            evs[2].record()
+        return enc
+
+    settle_steps = settle(step)
+    log("settled after %d untimed steps" % settle_steps)
     # plain device copy of the input: context for the roofline
     cpy = torch.empty_like(x)
     for _ in range(3):
@@ -577,17 +641,6 @@ def main():
     torch.cuda.synchronize()
     probe_GBps = 2 * n16 * 5 / (ce0.elapsed_time(ce1) * 1e-3) / 1e9
     del cpy
-
-    def step(evs=None):
-        if evs:
-            evs[0].record()
-        enc = pc.pc_encode(dcb, x, chunk, outs)
-        if evs:
-            evs[1].record()
-        decode(dcb, enc, out=dec_out, status=status)
-        if evs:
-            evs[2].record()
-        return enc
 
     log("warmup %d" % args.warmup)
     for _ in range(args.warmup):
@@ -686,6 +739,7 @@ def main():
 
     secondary = None
     if not args.no_secondary:
+        settle(lambda: pc.pc_histogram(x))
         hist_ms = time_calls(lambda: pc.pc_histogram(x), 10)
         secondary = {"histogram_GBps": round(n / (hist_ms * 1e-3) / 1e9, 1)}
         secondary["qlc_gelu_act"] = qlc_leg(pc, W, dev)
@@ -697,6 +751,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

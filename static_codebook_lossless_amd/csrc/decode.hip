@@ -895,8 +895,9 @@ __device__ __forceinline__ void decode_batch(const Leftovers &lo_, uint32_t nt, 
 // [0, n)), so no lane needs masking, then the workgroup's leftover groups.
 // Lanes of a corrupt sub-stream decode from somewhere in their segments (LDS
 // reads are clamped) and write unspecified bytes into their own 256-byte
-// range.  Three workgroups share a CU (LDS: the table and two segments of 33
-// words per lane; at most 168 VGPRs).
+// range.  Three workgroups share a CU (LDS: the table and one 41-word
+// segment slot per lane, which the two halves use in turn; at most 170
+// VGPRs).
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(
     const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
