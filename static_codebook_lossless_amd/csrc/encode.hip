@@ -269,6 +269,32 @@ __device__ __forceinline__ void place_group(uint64_t g, uint32_t ng, uint32_t p,
     atomicOr(&buf[wi + 2], __builtin_amdgcn_alignbit(lo, 0u, o));
 }
 
+// make_group without masking the lengths out of the entries: ng comes back
+// with the group's length in its low 16 bits and the sum of the four codes
+// above them (entries hold zeros in bits 8-15, so no carry reaches bit 16),
+// n23 likewise, and the 64-bit shift reads only the low 6 bits of its
+// count.  Callers mask the sum of a tile's four ng, and keep_groups takes
+// byte 0 of each.
+__device__ __forceinline__ void make_group_raw(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3, uint64_t &g,
+                                               uint32_t &ng) {
+    const uint32_t p01 = ((e0 >> 16) << (e1 & 31)) | (e1 >> 16);
+    const uint32_t p23 = ((e2 >> 16) << (e3 & 31)) | (e3 >> 16);
+    const uint32_t n23 = e2 + e3;
+    g = ((uint64_t)p01 << (n23 & 63)) | p23;
+    ng = e0 + e1 + n23;
+}
+
+template <class SH>
+__device__ __forceinline__ void lane_groups_raw(const uint4 &x, const SH &sh, uint64_t g[4], uint32_t ng[4]) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t v = w[q];
+        make_group_raw(sh.tab[v & 0xFF], sh.tab[(v >> 8) & 0xFF], sh.tab[(v >> 16) & 0xFF], sh.tab[v >> 24], g[q],
+                       ng[q]);
+    }
+}
+
 template <class SH>
 __device__ __forceinline__ void lane_groups(const uint4 &x, const SH &sh, uint64_t g[4], uint32_t ng[4]) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -530,8 +556,11 @@ struct UnitShared {
     uint32_t wtot[kUTiles * kUW];      // per (tile, wave): bits
     uint32_t misc[4];                  // [0] ticket of this unit, [1] of the next, [2..3] its word offset
     uint2 cmeta[2][kUTiles * kUW];     // per round (two in flight), chunk's first entry: (bits, first word)
+    uint32_t guard[4];                 // right before buf; its last two take zeros only (place_tile)
     uint32_t buf[kUBufW + 8];
 };
+static_assert(offsetof(UnitShared, buf) == offsetof(UnitShared, guard) + 16 && offsetof(UnitShared, buf) % 16 == 0,
+              "the guard words sit right before the buffer, which is cleared in 16-byte stores");
 
 // One lane's groups of one tile: two groups of <= 48 bits in three words (the
 // high 16 bits of both in the third), and the four group lengths in bytes.
@@ -547,7 +576,8 @@ __device__ __forceinline__ void keep_groups(const uint64_t (&g)[4], const uint32
         tg.w[3 * h + 1] = (uint32_t)g[2 * h + 1];
         tg.w[3 * h + 2] = (uint32_t)(g[2 * h] >> 32) | (uint32_t)(g[2 * h + 1] >> 32) << 16;
     }
-    tg.n = ng[0] | ng[1] << 8 | ng[2] << 16 | ng[3] << 24;
+    // byte 0 of each ng (the length; make_group_raw)
+    tg.n = __builtin_amdgcn_perm(ng[1], ng[0], 0x0C0C0400u) | __builtin_amdgcn_perm(ng[3], ng[2], 0x04000C0Cu);
     // the packed words are what stays live (the compiler would otherwise
     // keep the 64-bit groups and the unpacked counts instead)
 #pragma unroll
@@ -555,15 +585,24 @@ __device__ __forceinline__ void keep_groups(const uint64_t (&g)[4], const uint32
     asm volatile("" : "+v"(tg.n));
 }
 
-__device__ __forceinline__ void place_tile(const TileGroups &tg, uint32_t p, uint32_t *buf) {
+// Each group is placed from its end e (the bit after its last, buffer bit
+// 0 = MSB of buf[0]): the right-aligned group shifted left by 32 - e % 32
+// spans buffer words e / 32 - 2 .. e / 32, which are hi >> e,
+// alignbit(hi, lo, e) and alignbit(lo, 0, e) (the shifts read e % 32; for
+// e % 32 == 0 the last is zero).  base is the word two before buf[0] (in
+// UnitShared::guard): groups ending in buf's first two words OR their
+// zeros there.
+__device__ __forceinline__ void place_tile(const TileGroups &tg, uint32_t p, uint32_t *base) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const uint32_t h = q >> 1;
         const uint32_t hi = (q & 1) ? tg.w[3 * h + 2] >> 16 : tg.w[3 * h + 2] & 0xFFFF;
-        const uint64_t g = ((uint64_t)hi << 32) | tg.w[3 * h + (q & 1)];
-        const uint32_t ng = (tg.n >> (8 * q)) & 0xFF;
-        place_group(g, ng, p, buf);
-        p += ng;
+        const uint32_t lo = tg.w[3 * h + (q & 1)];
+        p += (tg.n >> (8 * q)) & 0xFF;
+        uint32_t *w = base + (p >> 5);
+        atomicOr(w, hi >> (p & 31));
+        atomicOr(w + 1, __builtin_amdgcn_alignbit(hi, lo, p));
+        atomicOr(w + 2, __builtin_amdgcn_alignbit(lo, 0u, p));
     }
 }
 
@@ -656,8 +695,8 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
                 // step ordered after the previous tile's packed groups
                 // (hoisting all lookups would keep 128 results live)
                 asm volatile("" : "+v"(x[r].x), "+v"(x[r].y), "+v"(x[r].z), "+v"(x[r].w));
-                lane_groups(x[r], sh, g, ng);
-                const uint32_t bits = ng[0] + ng[1] + ng[2] + ng[3];
+                lane_groups_raw(x[r], sh, g, ng);
+                const uint32_t bits = (ng[0] + ng[1] + ng[2] + ng[3]) & 0xFFFF;
                 const uint32_t incl = wave_incl_scan(bits);
                 if (ln == 63) sh.wtot[r * kUW + wave] = incl;
                 ex[r] = incl - bits;
@@ -727,7 +766,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
             // ---- phase 2: place every group, no barrier -----------------
 #pragma unroll
             for (uint32_t r = 0; r < kUTiles; ++r) {
-                place_tile(tg[r], pos[r], sh.buf);
+                place_tile(tg[r], pos[r], sh.guard + 2);
                 x[r] = load_stream16(nsrc + r * nstride);
                 asm volatile("" ::: "memory");
             }
@@ -741,7 +780,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
             if (wave == 0) unit_meta<E>(sh, slot, desc, s, words, ln, max_polls, status, chunk_bits, cwo, num_chunks);
             constexpr uint32_t kHalf = kUTiles / 2;
 #pragma unroll
-            for (uint32_t r = 0; r < kHalf; ++r) place_tile(tg[r], pos[r], sh.buf);
+            for (uint32_t r = 0; r < kHalf; ++r) place_tile(tg[r], pos[r], sh.guard + 2);
             __syncthreads();
             const uint64_t excl = unit_excl(sh);
             // unit word fb holds the bits of both halves; whole words
@@ -753,7 +792,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
             for (uint32_t i = tl; i <= fb + 2; i += kUT) sh.buf[i] = i == 0 ? carry : 0u;
             __syncthreads();
 #pragma unroll
-            for (uint32_t r = kHalf; r < kUTiles; ++r) place_tile(tg[r], pos[r] - fb * 32, sh.buf);
+            for (uint32_t r = kHalf; r < kUTiles; ++r) place_tile(tg[r], pos[r] - fb * 32, sh.guard + 2);
             __syncthreads();
             store_unit(sh.buf, payload + excl + fb, excl + fb, words - fb, tl);
 #pragma unroll
@@ -898,8 +937,8 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         uint64_t g[4];
         uint32_t ng[4];
         asm volatile("" : "+v"(x[r].x), "+v"(x[r].y), "+v"(x[r].z), "+v"(x[r].w));
-        lane_groups(x[r], sh, g, ng);
-        const uint32_t bits = ng[0] + ng[1] + ng[2] + ng[3];
+        lane_groups_raw(x[r], sh, g, ng);
+        const uint32_t bits = (ng[0] + ng[1] + ng[2] + ng[3]) & 0xFFFF;
         const uint32_t incl = wave_incl_scan(bits);
         if (lane == 63) sh.wtot[r * kUW + wave] = incl;
         ex[r] = incl - bits;
@@ -927,7 +966,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
     uint32_t *dst = payload + w0;
     if (nw <= kUBufW - 2) {
 #pragma unroll
-        for (uint32_t r = 0; r < kUTiles; ++r) place_tile(tg[r], p0 + pos[r], sh.buf);
+        for (uint32_t r = 0; r < kUTiles; ++r) place_tile(tg[r], p0 + pos[r], sh.guard + 2);
         __syncthreads();
         // the unit's first and last word may hold a neighbour's bits
         if (tid == 0) atomicOr(dst, sh.buf[0]);
@@ -938,7 +977,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         // two halves of four tiles
         constexpr uint32_t kHalf = kUTiles / 2;
 #pragma unroll
-        for (uint32_t r = 0; r < kHalf; ++r) place_tile(tg[r], p0 + pos[r], sh.buf);
+        for (uint32_t r = 0; r < kHalf; ++r) place_tile(tg[r], p0 + pos[r], sh.guard + 2);
         __syncthreads();
         const uint32_t fb = (p0 + (uint32_t)__builtin_amdgcn_readlane((int)exs, (int)(kHalf * kUW))) >> 5;
         if (tid == 0) atomicOr(dst, sh.buf[0]);
@@ -948,7 +987,7 @@ __global__ __launch_bounds__(kUT) __attribute__((amdgpu_waves_per_eu(4))) void e
         for (uint32_t i = tid; i <= fb + 2; i += kUT) sh.buf[i] = i == 0 ? carry : 0u;
         __syncthreads();
 #pragma unroll
-        for (uint32_t r = kHalf; r < kUTiles; ++r) place_tile(tg[r], p0 + pos[r] - fb * 32, sh.buf);
+        for (uint32_t r = kHalf; r < kUTiles; ++r) place_tile(tg[r], p0 + pos[r] - fb * 32, sh.guard + 2);
         __syncthreads();
         if (tid == kUT - 1) atomicOr(dst + nw - 1, sh.buf[nw - 1 - fb]);
         store_words(sh.buf, dst + fb, w0 + fb, 0, nw - 1 - fb, tid);
