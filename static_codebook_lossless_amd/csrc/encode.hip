@@ -239,6 +239,7 @@ struct ChunkShared {
     uint32_t tab[256];                    // code << 16 | length
     uint32_t wave_tot[NT][THREADS / 64];  // per tile, per wave: bits
     uint32_t misc[4];
+    uint32_t guard[4];                    // right before buf; its last two take zeros only (place_group_end)
     uint32_t buf[BUFW + 8];
 };
 
@@ -267,6 +268,20 @@ __device__ __forceinline__ void place_group(uint64_t g, uint32_t ng, uint32_t p,
     atomicOr(&buf[wi], hi >> o);
     atomicOr(&buf[wi + 1], __builtin_amdgcn_alignbit(hi, lo, o));
     atomicOr(&buf[wi + 2], __builtin_amdgcn_alignbit(lo, 0u, o));
+}
+
+// The same three ORs for a group given by its end e (the bit after its
+// last, bit 0 = MSB of the buffer's first word): the right-aligned group
+// (hi:lo) shifted left by 32 - e % 32 spans buffer words e / 32 - 2 ..
+// e / 32, which are hi >> e, alignbit(hi, lo, e) and alignbit(lo, 0, e)
+// (the shifts read e % 32; for e % 32 == 0 the last is zero).  base is the
+// word two before the buffer's first (the guard words before it take the
+// zeros of groups that end in its first two words).
+__device__ __forceinline__ void place_group_end(uint32_t hi, uint32_t lo, uint32_t e, uint32_t *base) {
+    uint32_t *w = base + (e >> 5);
+    atomicOr(w, hi >> (e & 31));
+    atomicOr(w + 1, __builtin_amdgcn_alignbit(hi, lo, e));
+    atomicOr(w + 2, __builtin_amdgcn_alignbit(lo, 0u, e));
 }
 
 // make_group without masking the lengths out of the entries: ng comes back
@@ -324,6 +339,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
     uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws,
     uint32_t *__restrict__ status, uint32_t max_polls) {
     using SH = ChunkShared<THREADS, NT, BUFW>;
+    static_assert(offsetof(SH, buf) == offsetof(SH, guard) + 16 && offsetof(SH, buf) % 16 == 0,
+                  "the guard words sit right before the buffer, which is cleared in 16-byte stores");
     constexpr uint32_t TILE = THREADS * kSymPerLane;
     constexpr uint32_t NW = THREADS / 64;
     constexpr int NC = NT / TPC;  // chunks per workgroup
@@ -369,8 +386,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
         if (r + 1 < NT) xn = load_stream16(src + (r + 1) * TILE);
         uint64_t g[4];
         uint32_t ng[4];
-        lane_groups(xc, sh, g, ng);
-        const uint32_t bits = ng[0] + ng[1] + ng[2] + ng[3];
+        lane_groups_raw(xc, sh, g, ng);
+        const uint32_t bits = (ng[0] + ng[1] + ng[2] + ng[3]) & 0xFFFF;
         const uint32_t incl = wave_incl_scan(bits);
         if (lane == 63) sh.wave_tot[r][wave] = incl;
         __syncthreads();
@@ -386,8 +403,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
         if (r < NT - kHold) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                place_group(g[q], ng[q], p, sh.buf);
-                p += ng[q];
+                p += ng[q] & 0xFF;
+                place_group_end((uint32_t)(g[q] >> 32), (uint32_t)g[q], p, sh.guard + 2);
             }
         } else {
             const int hr = r - (NT - kHold);  // unrolled: a constant
@@ -400,7 +417,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
             // formed here, not kept as table entries
             asm volatile("" : "+v"(HG[hr][0]), "+v"(HG[hr][1]), "+v"(HG[hr][2]), "+v"(HG[hr][3]), "+v"(HG[hr][4]),
                          "+v"(HG[hr][5]));
-            HN[hr] = ng[0] | ng[1] << 8 | ng[2] << 16 | ng[3] << 24;
+            HN[hr] = __builtin_amdgcn_perm(ng[1], ng[0], 0x0C0C0400u) | __builtin_amdgcn_perm(ng[3], ng[2], 0x04000C0Cu);
             HP[hr] = p;
         }
         tbase = uniform(tbase + ttot);
@@ -417,10 +434,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS
             for (int q = 0; q < 4; ++q) {
                 const uint32_t h = q >> 1;
                 const uint32_t hi = (q & 1) ? HG[hr][3 * h + 2] >> 16 : HG[hr][3 * h + 2] & 0xFFFF;
-                const uint64_t g = ((uint64_t)hi << 32) | HG[hr][3 * h + (q & 1)];
-                const uint32_t ng = (HN[hr] >> (8 * q)) & 0xFF;
-                place_group(g, ng, p, sh.buf);
-                p += ng;
+                p += (HN[hr] >> (8 * q)) & 0xFF;
+                place_group_end(hi, HG[hr][3 * h + (q & 1)], p, sh.guard + 2);
             }
         }
         __syncthreads();
@@ -585,13 +600,9 @@ __device__ __forceinline__ void keep_groups(const uint64_t (&g)[4], const uint32
     asm volatile("" : "+v"(tg.n));
 }
 
-// Each group is placed from its end e (the bit after its last, buffer bit
-// 0 = MSB of buf[0]): the right-aligned group shifted left by 32 - e % 32
-// spans buffer words e / 32 - 2 .. e / 32, which are hi >> e,
-// alignbit(hi, lo, e) and alignbit(lo, 0, e) (the shifts read e % 32; for
-// e % 32 == 0 the last is zero).  base is the word two before buf[0] (in
-// UnitShared::guard): groups ending in buf's first two words OR their
-// zeros there.
+// A tile's four groups from bit p on, each placed from its end
+// (place_group_end); base is the word two before buf[0] (in
+// UnitShared::guard).
 __device__ __forceinline__ void place_tile(const TileGroups &tg, uint32_t p, uint32_t *base) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -599,10 +610,7 @@ __device__ __forceinline__ void place_tile(const TileGroups &tg, uint32_t p, uin
         const uint32_t hi = (q & 1) ? tg.w[3 * h + 2] >> 16 : tg.w[3 * h + 2] & 0xFFFF;
         const uint32_t lo = tg.w[3 * h + (q & 1)];
         p += (tg.n >> (8 * q)) & 0xFF;
-        uint32_t *w = base + (p >> 5);
-        atomicOr(w, hi >> (p & 31));
-        atomicOr(w + 1, __builtin_amdgcn_alignbit(hi, lo, p));
-        atomicOr(w + 2, __builtin_amdgcn_alignbit(lo, 0u, p));
+        place_group_end(hi, lo, p, base);
     }
 }
 
