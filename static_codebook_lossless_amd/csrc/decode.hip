@@ -69,7 +69,9 @@ constexpr uint32_t kOffFlag = kOffLeft + 264;
 constexpr uint32_t kOffSlots = kOffLeft + 272;
 constexpr uint32_t kLdsBytes = kOffSlots + (kThreads * kSlotWords + 4) * 4;
 static_assert(kOffSlots % 16 == 0, "slots hold 16-byte quads for the output transpose");
-static_assert(kThreads * kSlotWords * 4 >= 4 * 8192, "the output transpose fits the slots");
+// each wave's output transpose (8 KiB) fits inside its own lanes' slots
+constexpr uint32_t kWaveSlotQuads = 64 * kSlotWords / 4;
+static_assert(64 * kSlotWords % 4 == 0 && kWaveSlotQuads * 16 >= 8192, "the output transpose fits a wave's slots");
 // three workgroups per CU, with room for an LDS allocation granularity of
 // 512 or 1280 bytes
 static_assert(3 * ((kLdsBytes + 1279) / 1280 * 1280) <= 160 * 1024, "three workgroups per CU");
@@ -410,15 +412,17 @@ __device__ __forceinline__ uint32_t decode_half(const LdsWords &src, uint32_t po
 }
 
 // A group's output goes out through LDS, half a sub-stream (128 bytes per
-// lane) at a time: each wave writes its lanes' 8 quads into its own 8 KiB
-// of the segment area, then reads them back so that every store
+// lane) at a time: each wave writes its lanes' 8 quads into the first 8 KiB
+// of its own lanes' segment slots, then reads them back so that every store
 // instruction writes eight whole 128-byte lines (8 lanes per line) instead of
 // 16 bytes into each of 64 lines.  Quad q of lane l sits at slot
-// l * 8 + (q ^ (l % 8)).
+// l * 8 + (q ^ (l % 8)).  A wave starts this as soon as its own lanes have
+// decoded their second halves: no other wave reads those slots by then
+// (window reads that run past a segment's end read words they never use).
 __device__ __forceinline__ void store_group(uint4 *buf, uint8_t *out, uint32_t tid, const uint32_t (&o1)[kHalfWords],
                                             const uint32_t (&o2)[kHalfWords]) {
     const uint32_t w = tid >> 6, l = tid & 63;
-    uint4 *wb = buf + w * 512;
+    uint4 *wb = buf + w * kWaveSlotQuads;
     uint8_t *wout = out + (size_t)w * 64 * kSub;
 #pragma unroll
     for (uint32_t h = 0; h < 2; ++h) {
@@ -720,8 +724,8 @@ __device__ __forceinline__ void decode_group_global(uint64_t grp, const Tables &
 //       segment and starts inside its second; the second-half segments are
 //       written into the segment area;
 //   B4  second half decoded; its steps issue the loads of the next group's
-//       first-half segments;
-//   B5  the output goes out through the segment area.
+//       first-half segments; then each wave, without waiting for the
+//       others, sends its lanes' output out through their slots.
 // A group where any lane's half does not fit its segment (more than ~9.8
 // bits per symbol over 128 symbols) is decoded again from global memory, and
 // nothing of the staged pass is stored.
@@ -838,7 +842,6 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
         });
         if (!gfail && sj.j.ok && (saw_invalid<MODE>(bad, t) || pos != sj.j.pos_want - sj.b * 32))
             flag_corrupt(status);
-        __syncthreads();  // B5: the slots take the output
         if (!gfail)
             store_group(reinterpret_cast<uint4 *>(slots), out + grp * kThreads * kSub, tid, o1, o2);
         else
