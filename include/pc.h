@@ -63,7 +63,7 @@ extern "C" {
 typedef enum pc_status {
     PC_OK = 0,
     PC_ERR_INVALID_ARG = 1, /* a pointer, size, alignment or enum is invalid */
-    PC_ERR_UNSUPPORTED = 2, /* valid request this build cannot serve */
+    PC_ERR_UNSUPPORTED = 2, /* valid request the library cannot serve */
     PC_ERR_CAPACITY = 3,    /* an output or workspace buffer is too small */
     PC_ERR_CORRUPT = 4,     /* data do not form a valid container (decode) */
     PC_ERR_HIP = 5,         /* the HIP runtime reported an error */
