@@ -1079,6 +1079,149 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Small chunks of any size (a multiple of 256 bytes below 32 KiB): a
+// workgroup takes K consecutive full chunks (K * chunk <= 64 KiB, K <= 64),
+// so that the cross-chunk scan runs once per K chunks instead of once per
+// chunk.  Two passes over the K chunks:
+//   1. count: every lane's 16 code lengths, summed over its row of 16 lanes
+//      (one 256-symbol sub-stream; rows and sub-streams coincide because a
+//      tile starts on a sub-stream); then one scan over the <= 256
+//      sub-streams gives each sub-stream's bit offset inside its chunk (the
+//      side index), each chunk's bit count and, by a wave scan over the K
+//      chunks' word counts, each chunk's first word relative to the first
+//      chunk; the look-back turns the K chunks' word total into their
+//      offset in the payload;
+//   2. pack: per tile of 4096 symbols, every lane's codewords are ORed into
+//      the staging words at its known bit position (chunk start word * 32 +
+//      sub-stream offset + the lane's offset in its row) and the tile's
+//      words are stored, the tile ending where the next one starts (so the
+//      zero padding after a chunk that ends inside a tile is stored with it).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kMultiMaxChunks = 64;
+constexpr uint32_t kMultiBytes = 65536;
+
+struct MultiShared {
+    // a tile spans <= 4096 * 12 bits, the padding of <= 16 chunk ends and the
+    // offset of its first bit in its first word; pack_lane may OR zeros two
+    // words past the last
+    static constexpr uint32_t kStage = kTile * PC_MAX_LEN / 32 + 16 + 8;
+    uint16_t code[256];
+    uint8_t len[256];
+    uint32_t wave_tot[kThreads / 64];
+    uint32_t sub_bits[kMultiBytes / kSub];  // per sub-stream of the K chunks
+    uint32_t sub_excl[kMultiBytes / kSub];  // bits before it, counted from the first chunk's start (no padding)
+    uint32_t rel[kMultiMaxChunks + 1];      // chunk j's first word relative to chunk 0's; [K] = the total
+    uint32_t misc[4];
+    uint32_t stage[kStage];
+};
+
+// Inclusive prefix sum over each row of 16 lanes.
+__device__ __forceinline__ uint32_t row_incl_scan(uint32_t v) {
+    v += dpp_u32<0x111>(v);  // row_shr:1
+    v += dpp_u32<0x112>(v);  // row_shr:2
+    v += dpp_u32<0x114>(v);  // row_shr:4
+    v += dpp_u32<0x118>(v);  // row_shr:8
+    return v;
+}
+
+// Bit position, relative to chunk 0's first word, of sub-stream s's first
+// bit (s below the K chunks' sub-stream count).
+__device__ __forceinline__ uint32_t multi_sub_pos(const MultiShared &sh, uint32_t s, uint32_t spc) {
+    const uint32_t j = s / spc;
+    return sh.rel[j] * 32 + (sh.sub_excl[s] - sh.sub_excl[j * spc]);
+}
+
+__global__ __launch_bounds__(kThreads) void encode_multi_kernel(
+    const pc_codebook *__restrict__ cb, const uint8_t *__restrict__ in, uint32_t chunk, uint32_t K,
+    uint32_t num_chunks, uint32_t *__restrict__ payload, uint32_t *__restrict__ chunk_bits,
+    uint64_t *__restrict__ cwo, uint32_t *__restrict__ sub_off, uint64_t *__restrict__ ws,
+    uint32_t *__restrict__ status, uint32_t max_polls) {
+    __shared__ MultiShared sh;
+    const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) sh.misc[0] = atomicAdd(reinterpret_cast<uint32_t *>(ws), 1u);
+    {
+        const uint8_t *cbb = reinterpret_cast<const uint8_t *>(cb);
+        sh.code[tid] = reinterpret_cast<const uint16_t *>(cbb + kOffCode)[tid];
+        sh.len[tid] = cbb[kOffLength + tid];
+    }
+    for (uint32_t i = tid; i < MultiShared::kStage; i += kThreads) sh.stage[i] = 0;
+    __syncthreads();
+    const uint32_t t = uniform(sh.misc[0]);  // look-back index; chunks t K .. t K + K - 1
+    const uint32_t c0 = t * K;
+    const uint64_t base = (uint64_t)c0 * chunk;
+    const uint32_t L = K * chunk;  // bytes of the K chunks (all full)
+    const uint32_t spc = chunk / kSub, nsub = L / kSub;
+    const uint32_t ntiles = (L + kTile - 1) / kTile;
+
+    // ---- 1. count: bits per sub-stream ------------------------------------
+    for (uint32_t r = 0; r < ntiles; ++r) {
+        const uint32_t off = r * kTile + tid * kSymPerLane;
+        const uint32_t valid = lane_valid(off, L);
+        const uint32_t row = row_incl_scan(lane_bits(load_lane(in, base, off, L), valid, sh));
+        const uint32_t s = r * (kTile / kSub) + (tid >> 4);
+        if ((tid & 15) == 15 && s < nsub) sh.sub_bits[s] = row;
+    }
+    __syncthreads();
+    const uint32_t bs = tid < nsub ? sh.sub_bits[tid] : 0u;
+    const uint32_t incl = wave_incl_scan(bs);
+    if (lane == 63) sh.wave_tot[wave] = incl;
+    __syncthreads();
+    const uint32_t sx = incl - bs + (wave > 0 ? sh.wave_tot[0] : 0u) + (wave > 1 ? sh.wave_tot[1] : 0u) +
+                        (wave > 2 ? sh.wave_tot[2] : 0u);
+    sh.sub_excl[tid] = sx;
+    __syncthreads();
+    if (tid < nsub) {
+        const uint32_t j = tid / spc, first = j * spc;
+        const uint32_t in_chunk = sx - sh.sub_excl[first];
+        sub_off[(uint64_t)c0 * spc + tid] = in_chunk;
+        if (tid - first == spc - 1) {
+            const uint32_t bits = in_chunk + bs;
+            chunk_bits[c0 + j] = bits;
+            sh.rel[j] = (bits + 31) >> 5;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const uint32_t wj = lane < K ? sh.rel[lane] : 0u;
+        const uint32_t wi = wave_incl_scan(wj);
+        const uint32_t W = uniform((uint32_t)__shfl(wi, 63, 64));
+        const uint64_t excl = lookback(ws + 1, t, W, lane, max_polls, status);
+        if (lane < K) {
+            cwo[c0 + lane] = excl + (wi - wj);
+            sh.rel[lane] = wi - wj;
+        }
+        if (lane == 0) {
+            sh.rel[K] = W;
+            if (c0 + K == num_chunks) cwo[num_chunks] = excl + W;
+            sh.misc[1] = (uint32_t)excl;
+            sh.misc[2] = (uint32_t)(excl >> 32);
+        }
+    }
+    __syncthreads();
+    uint32_t *dst = payload + (((uint64_t)sh.misc[2] << 32) | sh.misc[1]);
+    const uint32_t total_bits = sh.rel[K] * 32;
+
+    // ---- 2. pack ------------------------------------------------------------
+    for (uint32_t r = 0; r < ntiles; ++r) {
+        const uint32_t off = r * kTile + tid * kSymPerLane;
+        const uint32_t valid = lane_valid(off, L);
+        const uint4 x = load_lane(in, base, off, L);
+        const uint32_t b = lane_bits(x, valid, sh);
+        const uint32_t rowx = row_incl_scan(b) - b;
+        const uint32_t s0 = r * (kTile / kSub);
+        const uint32_t tbeg = uniform(multi_sub_pos(sh, s0, spc));
+        const uint32_t s1 = s0 + kTile / kSub;
+        const uint32_t tend = uniform(s1 < nsub ? multi_sub_pos(sh, min(s1, nsub - 1), spc) : total_bits);
+        const uint32_t s = min(s0 + (tid >> 4), nsub - 1);
+        // a lane past the end ORs zeros at the stage's start
+        const uint32_t p = valid ? multi_sub_pos(sh, s, spc) + rowx - (tbeg & ~31u) : 0u;
+        pack_lane(x, valid, p, sh);
+        __syncthreads();
+        flush_tile<kThreads>(sh, dst, tbeg, tend, r + 1 == ntiles, tid);
+    }
+}
+
 // Zero the ticket, the look-back descriptors and the status word; write the
 // total-word entry for an empty input.
 __global__ void encode_init_kernel(uint64_t *ws, uint64_t ws_words, uint64_t *cwo, int empty, uint32_t *status) {
@@ -1109,6 +1252,9 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
     //   - power-of-two chunks of 1 .. 64 KiB on large inputs: the persistent
     //     unit kernel (64 KiB units of whole chunks);
     //   - multiples of 64 KiB above it: count, scan and place launches;
+    //   - other chunks of at most 32 KiB: K consecutive chunks per
+    //     workgroup (encode_multi_kernel), unless they are 4 .. 64 KiB
+    //     powers of two:
     //   - otherwise 4 .. 64 KiB chunks: workgroups of NT tiles (TPC tiles per
     //     chunk, so NT / TPC consecutive chunks and one look-back per
     //     workgroup).  The 1024-lane kernels hold 64K symbols per
@@ -1130,6 +1276,18 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
                                stream, cb, in, n, chunk, (uint32_t)nc, payload, chunk_bits, cwo, sub_off,  \
                                ws, status, max_polls);                                                     \
             done = nsup * ((NT) / (TPC));                                                                  \
+            tickets = nsup;                                                                                \
+        }                                                                                               \
+    } while (0)
+#define PC_ENC_MULTI()                                                                                     \
+    do {                                                                                                   \
+        const uint32_t K = kMultiBytes / chunk < kMultiMaxChunks ? kMultiBytes / chunk : kMultiMaxChunks;  \
+        const uint64_t nsup = nfull / K;                                                                   \
+        if (nsup) {                                                                                        \
+            hipLaunchKernelGGL(encode_multi_kernel, dim3((uint32_t)nsup), dim3(kThreads), 0, stream, cb, in, \
+                               chunk, K, (uint32_t)nc, payload, chunk_bits, cwo, sub_off, ws, status,      \
+                               max_polls);                                                                 \
+            done = nsup * K;                                                                               \
             tickets = nsup;                                                                                \
         }                                                                                               \
     } while (0)
@@ -1191,6 +1349,7 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
     else if (chunk == 8192) PC_ENC(256, 2, 3072, 2);
     else if (chunk == 4096 && nfull >= kManySmall) PC_ENC(256, 8, 8200, 1);
     else if (chunk == 4096) PC_ENC(256, 1, 1536, 1);
+    else if (2 * chunk <= kMultiBytes) PC_ENC_MULTI();
     const uint64_t rest = nc - done;
     // look-back indices continue from the multi-chunk launch's: after the
     // chunk kernels (which take exactly `tickets` tickets from counter 0)
@@ -1209,6 +1368,7 @@ hipError_t launch_encode(const pc_codebook *cb, const uint8_t *in, uint64_t n, u
                            (uint32_t)cbase, status, max_polls);
     }
 #undef PC_ENC
+#undef PC_ENC_MULTI
 #undef PC_ENC_UNIT
     return hipGetLastError();
 }

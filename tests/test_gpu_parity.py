@@ -323,6 +323,31 @@ def test_many_small_chunks(chunk):
     roundtrip(dcb, obook, x_np, chunk)
 
 
+@pytest.mark.parametrize("chunk", [256, 512, 768, 1024, 2048, 3072, 12288, 20480, 32512])
+def test_small_chunks_several_per_workgroup(chunk):
+    """Chunks below 32 KiB that no specialised encoder takes (not a power of
+    two, or a power of two below 4 KiB on a small input) go K to a workgroup
+    (K * chunk <= 64 KiB, K <= 64): three and a half workgroups' worth of
+    skewed data, then whole chunks and a short chunk for the re-reading
+    kernel; then a run where every other chunk is uniform bytes (about 10
+    bits per symbol under this code, so tiles span the most words), and one
+    of 2 MB."""
+    dcb, obook = make_book(np.bincount(skewed(1 << 20, 98), minlength=256))
+    K = min(64, 65536 // chunk)
+    rng = np.random.default_rng(chunk)
+    n = 3 * K * chunk + (K // 2) * chunk + 5 * chunk + 100
+    say("several chunks per workgroup:", chunk, "K", K, "n", n)
+    roundtrip(dcb, obook, skewed(n, chunk + 1), chunk)
+    x_np = skewed(n, chunk + 2)
+    for c in range(0, n // chunk, 2):
+        x_np[c * chunk:(c + 1) * chunk] = rng.integers(0, 256, chunk, dtype=np.uint8)
+    say("several chunks per workgroup, mixed:", chunk)
+    roundtrip(dcb, obook, x_np, chunk)
+    n2 = 2_000_000
+    say("several chunks per workgroup, 2 MB:", chunk)
+    roundtrip(dcb, obook, skewed(n2, chunk + 3), chunk)
+
+
 @pytest.mark.parametrize("kind", ["huffman", "qlc"])
 def test_degenerate_data(kind):
     bits = (1, 3, 3, 3, 3, 5, 6, 7) if kind == "qlc" else None
