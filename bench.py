@@ -188,9 +188,10 @@ SQ_RATIOS = [
 ]
 
 
-def sq_summary(dirs, out, commands):
-    """Median per-dispatch SQ counters of the coder kernels, from one or more
-    rocprofv3 --pmc runs, and the ratios in SQ_RATIOS."""
+def counter_summary(dirs, out, commands, title, self_cmd, ratios, shares=()):
+    """Median per-dispatch counters of the coder kernels, from one or more
+    rocprofv3 --pmc runs; `ratios` divides two counters, `shares` gives
+    a / (a + b)."""
     vals = {}
     for d in dirs:
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -204,22 +205,39 @@ def sq_summary(dirs, out, commands):
                     if kname in r["Kernel_Name"]:
                         vals.setdefault(kind, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     med = {k: {c: sorted(v)[len(v) // 2] for c, v in cs.items()} for k, cs in vals.items()}
-    lines = ["# SQ counters of the coder kernels on the 1 GiB e4m3 stream (64 KiB chunks, Huffman-12),",
-             "# median over dispatches, summed over the device.",
-             "# Commands (from the repository root, after cd /tmp && export TMPDIR=/tmp):"]
+    lines = list(title) + ["# Commands (from the repository root, after cd /tmp && export TMPDIR=/tmp):"]
     lines += ["#   " + c for c in commands]
-    lines.append("#   python3 bench.py --sq-summary " + " ".join(dirs))
+    lines.append("#   python3 bench.py " + self_cmd + " " + " ".join(dirs))
     kinds = [k for k in KERNEL_NAMES if k in med]
     counters = sorted({c for k in kinds for c in med[k]})
     lines.append("%-44s " % "counter" + " ".join("%18s" % k for k in kinds))
     for c in counters:
         lines.append("%-44s " % c + " ".join("%18.0f" % med[k].get(c, float("nan")) for k in kinds))
-    for label, a, b in SQ_RATIOS:
+    for label, a, b in ratios:
         if all(a in med[k] and b in med[k] and med[k][b] for k in kinds):
             lines.append("%-44s " % label + " ".join("%18.4f" % (med[k][a] / med[k][b]) for k in kinds))
+    for label, a, b in shares:
+        if all(a in med[k] and b in med[k] and med[k][a] + med[k][b] for k in kinds):
+            lines.append("%-44s " % label + " ".join("%18.4f" % (med[k][a] / (med[k][a] + med[k][b])) for k in kinds))
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def sq_summary(dirs, out, commands):
+    """Median per-dispatch SQ counters of the coder kernels, and the ratios
+    in SQ_RATIOS."""
+    counter_summary(dirs, out, commands,
+                    ["# SQ counters of the coder kernels on the 1 GiB e4m3 stream (64 KiB chunks, Huffman-12),",
+                     "# median over dispatches, summed over the device."], "--sq-summary", SQ_RATIOS)
+
+
+def l2_summary(dirs, out, commands):
+    """Median per-dispatch L2 (TCC) hits and misses of the coder kernels."""
+    counter_summary(dirs, out, commands,
+                    ["# L2 (TCC) requests of the coder kernels on the 1 GiB e4m3 stream (64 KiB chunks, Huffman-12),",
+                     "# median over dispatches, summed over the device's TCC channels."], "--l2-summary", [],
+                    [("L2 hit share of requests", "TCC_HIT_sum", "TCC_MISS_sum")])
 
 
 def load_traffic(kind):
@@ -539,7 +557,9 @@ def main():
     ap.add_argument("--trace-last", type=int, default=0,
                     help="with --trace-summary: also the mean of each coder kernel's last N dispatches")
     ap.add_argument("--sq-summary", nargs="+", metavar="PMC_DIR")
-    ap.add_argument("--sq-commands", nargs="*", default=[])
+    ap.add_argument("--l2-summary", nargs="+", metavar="PMC_DIR")
+    ap.add_argument("--sq-commands", nargs="*", default=[],
+                    help="with --sq-summary or --l2-summary: the profiler commands, recorded in the file")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the QLC (GELU tensor) and histogram measurements")
     ap.add_argument("--no-configs", action="store_true",
@@ -554,6 +574,10 @@ def main():
         return 0
     if args.sq_summary:
         sq_summary(args.sq_summary, os.path.join(ROOT, "profiles", "coder_kernels_stream_1g_sq_counters.txt"),
+                   args.sq_commands)
+        return 0
+    if args.l2_summary:
+        l2_summary(args.l2_summary, os.path.join(ROOT, "profiles", "coder_kernels_stream_1g_l2_hits.txt"),
                    args.sq_commands)
         return 0
     if args.pmc_summary:

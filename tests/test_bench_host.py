@@ -84,3 +84,28 @@ def test_pmc_summary_scales_by_the_probe_copy(tmp_path):
     assert abs(float(kern["encode"][5]) - 600.0 * 1024 * 2) < 1
     assert abs(float(kern["encode"][7]) - 800.0 * 1024 * 1.024) < 1
     assert abs(float(kern["decode"][5]) - 410.0 * 1024 * 2) < 1  # the median dispatch
+
+
+def test_l2_summary_medians_and_hit_share(tmp_path):
+    """L2 counter table on a hand-made rocprofv3 CSV: per kernel the median
+    over dispatches of each counter, and hits / (hits + misses)."""
+    import csv
+
+    d = tmp_path / "l2"
+    d.mkdir()
+    rows = [("pc::encode_unit_kernel<64>(...)", "TCC_HIT_sum", v) for v in (90.0, 80.0, 70.0)]
+    rows += [("pc::encode_unit_kernel<64>(...)", "TCC_MISS_sum", v) for v in (10.0, 20.0, 30.0)]
+    rows += [("pc::decode_kernel<0>(...)", "TCC_HIT_sum", 50.0), ("pc::decode_kernel<0>(...)", "TCC_MISS_sum", 150.0)]
+    rows += [("__amd_rocclr_copyBuffer", "TCC_HIT_sum", 1.0)]
+    with open(d / "bench_counter_collection.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for k, c, v in rows:
+            wr.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+    out = tmp_path / "l2.txt"
+    bench.l2_summary([str(d)], str(out), ["rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum -- python3 bench.py"])
+    lines = {l.split()[0]: l.split() for l in out.read_text().splitlines() if not l.startswith("#")}
+    assert lines["counter"][1:] == ["encode", "decode"]
+    assert lines["TCC_HIT_sum"][1:] == ["80", "50"] and lines["TCC_MISS_sum"][1:] == ["20", "150"]
+    share = [l for l in out.read_text().splitlines() if l.startswith("L2 hit share")][0].split()
+    assert share[-2:] == ["0.8000", "0.2500"]
