@@ -40,7 +40,7 @@ KERNEL_SOURCES = {
     "encode": os.path.join(ROOT, "static_codebook_lossless_amd", "csrc", "encode.hip"),
     "decode": os.path.join(ROOT, "static_codebook_lossless_amd", "csrc", "decode.hip"),
 }
-KERNEL_NAMES = {"encode": "encode_unit_kernel", "decode": "decode_kernel<0>"}
+KERNEL_NAMES = {"encode": "encode_unit_kernel", "decode": "decode_kernel<0, true>"}
 
 
 def log(*a):

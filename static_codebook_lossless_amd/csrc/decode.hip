@@ -58,6 +58,9 @@ constexpr uint32_t kLutBytes = 8192;
 constexpr uint32_t kLutOff = 19;  // entry = (19 - length) | symbol << 8
 constexpr uint32_t kLutMask = 0x1FFE;
 constexpr uint32_t kGroupsPerCU = 3;
+// inputs from this size on decode with streaming (non-temporal) second-half
+// segment loads and output stores (see seg_fetch)
+constexpr uint64_t kStreamBytes = 256ull << 20;
 // LDS layout (bytes): the table, the two segment-start tables (this group's
 // second halves, the next group's first halves), the leftover list and the
 // group-failure flag, then the slots (16-byte aligned: the output transpose
@@ -415,10 +418,12 @@ __device__ __forceinline__ uint32_t decode_half(const LdsWords &src, uint32_t po
 // lane) at a time: each wave writes its lanes' 8 quads into the first 8 KiB
 // of its own lanes' segment slots, then reads them back so that every store
 // instruction writes eight whole 128-byte lines (8 lanes per line) instead of
-// 16 bytes into each of 64 lines.  Quad q of lane l sits at slot
+// 16 bytes into each of 64 lines; with STREAM the stores are non-temporal
+// (the output is not read again here).  Quad q of lane l sits at slot
 // l * 8 + (q ^ (l % 8)).  A wave starts this as soon as its own lanes have
 // decoded their second halves: no other wave reads those slots by then
 // (window reads that run past a segment's end read words they never use).
+template <bool STREAM>
 __device__ __forceinline__ void store_group(uint4 *buf, uint8_t *out, uint32_t tid, const uint32_t (&o1)[kHalfWords],
                                             const uint32_t (&o2)[kHalfWords]) {
     const uint32_t w = tid >> 6, l = tid & 63;
@@ -435,7 +440,14 @@ __device__ __forceinline__ void store_group(uint4 *buf, uint8_t *out, uint32_t t
 #pragma unroll
         for (uint32_t t = 0; t < 8; ++t) {
             const uint32_t L = 8 * t + (l >> 3), Q = l & 7;
-            *reinterpret_cast<uint4 *>(wout + L * kSub + h * kHalf + Q * 16) = wb[L * 8 + (Q ^ (L & 7))];
+            const uint4 v = wb[L * 8 + (Q ^ (L & 7))];
+            uint8_t *dst = wout + L * kSub + h * kHalf + Q * 16;
+            if (STREAM) {
+                const u32x4 w4 = {v.x, v.y, v.z, v.w};
+                __builtin_nontemporal_store(w4, reinterpret_cast<u32x4 *>(dst));
+            } else {
+                *reinterpret_cast<uint4 *>(dst) = v;
+            }
         }
     }
 }
@@ -557,11 +569,19 @@ __device__ __forceinline__ gword *opaque_words(const uint32_t *p) {
 }
 
 // Load k of a set (k = 0..9); `start` is the start of the segment quad k
-// belongs to (read from the table a step earlier).
+// belongs to (read from the table a step earlier).  On inputs larger than
+// the 256 MB MALL (STREAM), the second-half sets, the last reads of their
+// lines, load non-temporally, as the output is stored: the L2 then keeps
+// the lines the first-half loads brought in, most of which the second-half
+// loads of the same group read again half a group later (a sub-stream's
+// first-half segment covers about three quarters of its words).  On
+// smaller inputs both stay ordinary (measured faster there).
+template <bool STREAM>
 __device__ __forceinline__ void seg_fetch(SegFetch &f, uint32_t k, uint32_t start, gword *gb, uint32_t pwr,
                                           uint32_t tid) {
     const uint32_t r = min(start + 4 * part_of(k, tid), pwr - 4);
-    const u32x4w v = *(gquadw *)((const __attribute__((address_space(1))) uint8_t *)gb + (r << 2));
+    gquadw *p = (gquadw *)((const __attribute__((address_space(1))) uint8_t *)gb + (r << 2));
+    const u32x4w v = STREAM ? __builtin_nontemporal_load(p) : *p;
     f.q[k] = make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -729,7 +749,7 @@ __device__ __forceinline__ void decode_group_global(uint64_t grp, const Tables &
 // A group where any lane's half does not fit its segment (more than ~9.8
 // bits per symbol over 128 symbols) is decoded again from global memory, and
 // nothing of the staged pass is stored.
-template <int MODE, bool CHECK>
+template <int MODE, bool CHECK, bool STREAM>
 __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const Tables &t, bool kind_ok,
                                               uint8_t *lds, const uint32_t *payload, uint64_t payload_words,
                                               const uint32_t *chunk_bits, const uint64_t *cwo,
@@ -759,7 +779,7 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
         const uint32_t pwr = words_left(wbase, payload_words);
 #pragma unroll
         for (uint32_t k = 0; k < kSetLoads; ++k)
-            seg_fetch(pf, k, starts_a[seg_of(k, tid0)], gb, pwr, tid0);
+            seg_fetch<false>(pf, k, starts_a[seg_of(k, tid0)], gb, pwr, tid0);
     }
     uint32_t o1[kHalfWords], o2[kHalfWords];
 
@@ -803,7 +823,7 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
         uint32_t st = starts_b[seg_of(0, tid)];
         uint32_t pos = decode_half<MODE, CHECK>(src, sj.j.pos0 & 31, t, bad, o1, [&](uint32_t q) {
             if (q < kSetLoads) {
-                seg_fetch(pf, q, st, gb, pwr, tid);
+                seg_fetch<STREAM>(pf, q, st, gb, pwr, tid);
                 if (q + 1 < kSegQuads) st = starts_b[seg_of(q + 1, tid)];
             }
         });
@@ -836,14 +856,14 @@ __device__ __forceinline__ void decode_groups(uint64_t grp, uint32_t tid0, const
         st = starts_a[seg_of(0, tid)];
         pos = decode_half<MODE, CHECK>(src, pos2, t, bad, o2, [&](uint32_t q) {
             if (q < kSetLoads) {
-                seg_fetch(pf, q, st, ngb, npwr, tid);
+                seg_fetch<false>(pf, q, st, ngb, npwr, tid);
                 if (q + 1 < kSegQuads) st = starts_a[seg_of(q + 1, tid)];
             }
         });
         if (!gfail && sj.j.ok && (saw_invalid<MODE>(bad, t) || pos != sj.j.pos_want - sj.b * 32))
             flag_corrupt(status);
         if (!gfail)
-            store_group(reinterpret_cast<uint4 *>(slots), out + grp * kThreads * kSub, tid, o1, o2);
+            store_group<STREAM>(reinterpret_cast<uint4 *>(slots), out + grp * kThreads * kSub, tid, o1, o2);
         else
             decode_group_global<MODE>(grp, t, kind_ok, payload, payload_words, chunk_bits, cwo, sub_off, n, chunk,
                                       num_sub, num_chunks, out, status, tid);
@@ -901,7 +921,7 @@ __device__ __forceinline__ void decode_batch(const Leftovers &lo_, uint32_t nt, 
 // range.  Three workgroups share a CU (LDS: the table and one 41-word
 // segment slot per lane, which the two halves use in turn; at most 170
 // VGPRs).
-template <int MODE>
+template <int MODE, bool STREAM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void decode_kernel(
     const pc_codebook *__restrict__ cb, const uint32_t *__restrict__ payload, uint64_t payload_words,
     const uint32_t *__restrict__ chunk_bits, const uint64_t *__restrict__ cwo,
@@ -929,10 +949,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const uint64_t grp = blockIdx.x;
     if (grp < num_full) {
         if (cbp->complete == 1)
-            decode_groups<MODE, false>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo, sub_off,
+            decode_groups<MODE, false, STREAM>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo, sub_off,
                                        n, chunk, num_sub, num_full, num_chunks, out, status);
         else
-            decode_groups<MODE, true>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo, sub_off, n,
+            decode_groups<MODE, true, STREAM>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo, sub_off, n,
                                       chunk, num_sub, num_full, num_chunks, out, status);
     }
     __syncthreads();  // the tables are in LDS
@@ -1010,6 +1030,7 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     uint64_t grid_g = (uint64_t)num_cus * kGroupsPerCU;
     if (grid_g > num_groups) grid_g = num_groups;
     if (num_sub >= kMaxDecodeSubstreams) return hipErrorInvalidValue;  // the entry point checks first
+    const bool streaming = n >= kStreamBytes;
 #define PC_DEC(K)                                                                                             \
     hipLaunchKernelGGL(K, dim3((uint32_t)grid), dim3(kThreads), 0, stream, cb, payload, payload_words,         \
                        chunk_bits, cwo, sub_off, n, chunk, num_sub, num_full, nc, num_groups, out, status)
@@ -1019,10 +1040,12 @@ hipError_t launch_decode(int mode, const pc_codebook *cb, const uint32_t *payloa
     // with a full group the main kernel also takes the leftover groups;
     // without one, only the leftover kernel runs
     if (mode == kDecodeLut12) {
-        if (grid) PC_DEC(decode_kernel<kDecodeLut12>);
+        if (grid && streaming) PC_DEC((decode_kernel<kDecodeLut12, true>));
+        else if (grid) PC_DEC((decode_kernel<kDecodeLut12, false>));
         else PC_DEC_G(decode_global_kernel<kDecodeLut12>);
     } else {
-        if (grid) PC_DEC(decode_kernel<kDecodeQlc>);
+        if (grid && streaming) PC_DEC((decode_kernel<kDecodeQlc, true>));
+        else if (grid) PC_DEC((decode_kernel<kDecodeQlc, false>));
         else PC_DEC_G(decode_global_kernel<kDecodeQlc>);
     }
 #undef PC_DEC

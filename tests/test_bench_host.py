@@ -59,10 +59,10 @@ def test_pmc_summary_scales_by_the_probe_copy(tmp_path):
     cb_ = 1 << 20
     rows = {  # KiB per dispatch
         "FETCH_SIZE": [("__amd_rocclr_copyBuffer", 512.0), ("pc::probe_copy_kernel(...)", 512.0),
-                       ("pc::encode_unit_kernel<8>(...)", 600.0), ("pc::decode_kernel<0>(...)", 400.0),
-                       ("pc::decode_kernel<0>(...)", 420.0), ("pc::decode_kernel<0>(...)", 410.0)],
+                       ("pc::encode_unit_kernel<8>(...)", 600.0), ("pc::decode_kernel<0, true>(...)", 400.0),
+                       ("pc::decode_kernel<0, true>(...)", 420.0), ("pc::decode_kernel<0, true>(...)", 410.0)],
         "WRITE_SIZE": [("__amd_rocclr_copyBuffer", 1024.0), ("pc::probe_copy_kernel(...)", 1000.0),
-                       ("pc::encode_unit_kernel<8>(...)", 800.0), ("pc::decode_kernel<0>(...)", 1024.0)],
+                       ("pc::encode_unit_kernel<8>(...)", 800.0), ("pc::decode_kernel<0, true>(...)", 1024.0)],
     }
     dirs = {}
     for counter, rs in rows.items():
@@ -95,7 +95,7 @@ def test_l2_summary_medians_and_hit_share(tmp_path):
     d.mkdir()
     rows = [("pc::encode_unit_kernel<64>(...)", "TCC_HIT_sum", v) for v in (90.0, 80.0, 70.0)]
     rows += [("pc::encode_unit_kernel<64>(...)", "TCC_MISS_sum", v) for v in (10.0, 20.0, 30.0)]
-    rows += [("pc::decode_kernel<0>(...)", "TCC_HIT_sum", 50.0), ("pc::decode_kernel<0>(...)", "TCC_MISS_sum", 150.0)]
+    rows += [("pc::decode_kernel<0, true>(...)", "TCC_HIT_sum", 50.0), ("pc::decode_kernel<0, true>(...)", "TCC_MISS_sum", 150.0)]
     rows += [("__amd_rocclr_copyBuffer", "TCC_HIT_sum", 1.0)]
     with open(d / "bench_counter_collection.csv", "w", newline="") as f:
         wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
