@@ -127,6 +127,31 @@ def test_stream_1g_full_size():
     assert int(host(enc)["chunk_bits"].astype(np.int64).sum()) == cb.coded_bits(xc, obook["lengths"])
 
 
+def test_large_qlc_stream_both_decoders():
+    """A 300 MB stream under a QLC code (an incomplete code: both decoders
+    test every codeword for validity) at the size where the decoders stream
+    their second-half loads and output stores: the whole stream against the
+    oracle, and both decoders back to the input."""
+    bits = (1, 3, 3, 3, 3, 5, 6, 7)
+    n = 300_000_000 + 123
+    say("large QLC stream: generating", n)
+    x_np = skewed(n, 71)
+    dcb, obook = make_book(np.bincount(x_np[: 1 << 24], minlength=256), "qlc", bits)
+    assert pc.codebook_fields(dcb)["complete"] == 0  # Kraft sum 511/512
+    x, enc = gpu_encode(dcb, x_np, 65536)
+    say("large QLC stream: oracle encode")
+    want = coder.encode(x_np, obook["lengths"], obook["codes"], 65536, threads=16)
+    assert_same_stream(host(enc), want)
+    del want
+    for name, fn in (("pc_decode", pc.pc_decode), ("pc_decode_qlc", pc.pc_decode_qlc)):
+        say("large QLC stream:", name)
+        out, status = fn(dcb, enc)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert torch.equal(out, x)
+        del out
+
+
 @pytest.mark.parametrize("chunk", [65536, 32768, 16384, 8192, 4096, 2048, 1024])
 def test_persistent_unit_path(chunk):
     """Inputs large enough for the persistent 64 KiB-unit encoder (four
