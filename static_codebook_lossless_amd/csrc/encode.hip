@@ -1080,7 +1080,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel_any(
 }
 
 // ---------------------------------------------------------------------------
-// Small chunks of any size (a multiple of 256 bytes below 32 KiB): a
+// Small chunks of any size (a multiple of 256 bytes, at most 32 KiB): a
 // workgroup takes K consecutive full chunks (K * chunk <= 64 KiB, K <= 64),
 // so that the cross-chunk scan runs once per K chunks instead of once per
 // chunk.  Two passes over the K chunks:
