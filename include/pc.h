@@ -107,16 +107,17 @@ const char *pc_status_string(int status);
 /*
  * Build a fixed codebook on the host.  Pure, deterministic, thread-safe.
  *
- * counts: the pooled histogram of previous batches (first page, abstract:
- *   the average distribution of previous data batches; pooling equal-size
- *   batches by summing counts is proportional to averaging their PMFs).
+ * counts: the pooled histogram of previous batches ("Single-Stage Huffman
+ *   Encoder for ML Compression", abstract: the average distribution of
+ *   previous data batches; pooling equal-size batches by summing counts is
+ *   proportional to averaging their PMFs).
  * kind = PC_CODEBOOK_HUFFMAN: weights max(count,1) (every byte stays
  *   codable), package-merge length-limited to 12 bits (on equal weight a leaf
  *   precedes a package; leaves ordered by (weight, byte value)), then
  *   canonical codes in (length, byte value) order.  qlc_bits must be NULL.
  * kind = PC_CODEBOOK_QLC: qlc_bits[a] (0..9) is the index width of area a
- *   (second page, Tables 1 and 2); the areas must cover 256 ranks
- *   (sum 2^b >= 256).  Ranks order bytes by descending count, equal counts
+ *   ("Quad Length Codes for Lossless Compression of e4m3", Tables 1 and 2);
+ *   the areas must cover 256 ranks (sum 2^b >= 256).  Ranks order bytes by descending count, equal counts
  *   by lower byte value; the byte of rank r in area a gets code
  *   (a << b_a) | (r - start_a) of length 3 + b_a.
  * Returns PC_ERR_INVALID_ARG for NULL pointers, an unknown kind, or bad
@@ -127,9 +128,9 @@ pc_status pc_codebook_build(const uint64_t counts[256], int kind, const uint8_t 
 
 /*
  * Host check of a codebook blob (magic, version, lengths, tables).  The
- * pages define no codebook format (the single-stage page, abstract, only
- * requires that encoder and decoder hold the same precomputed codebook);
- * this checks the library's own layout above.
+ * pages define no codebook format ("Single-Stage Huffman Encoder for ML
+ * Compression", abstract, only requires that encoder and decoder hold the
+ * same precomputed codebook); this checks the library's own layout above.
  */
 pc_status pc_codebook_validate(const pc_codebook *cb);
 
@@ -137,8 +138,9 @@ pc_status pc_codebook_validate(const pc_codebook *cb);
  * Choose QLC area widths for a histogram: the 8 widths (each 0..9, areas
  * covering 256 ranks) that minimise sum(count * (3 + b_area(rank))) over the
  * ranked histogram, by dynamic programming over contiguous rank ranges --
- * the second page notes the scheme adapts to the distribution.  Ties keep
- * the lexicographically smallest width vector.  Host only.
+ * "Quad Length Codes for Lossless Compression of e4m3" (abstract) notes
+ * that the scheme adapts to the distribution.  Ties keep the
+ * lexicographically smallest width vector.  Host only.
  */
 pc_status pc_qlc_optimal_bits(const uint64_t counts[256], uint8_t bits_out[8]);
 
@@ -287,9 +289,10 @@ pc_status pc_decode(const pc_codebook *d_cb, const uint32_t *d_payload, size_t p
                     uint32_t *d_status, void *stream);
 
 /*
- * Decode a QLC-coded stream the way the second page describes the decoder:
- * read the 3-bit area number, read that area's fixed-width index, map the
- * rank to the symbol through the 256-entry table.  Same arguments, container
+ * Decode a QLC-coded stream the way "Quad Length Codes for Lossless
+ * Compression of e4m3" (abstract) describes its decoder: read the 3-bit
+ * area number, read that area's fixed-width index, map the rank to the
+ * symbol through the 256-entry table.  Same arguments, container
  * and error rules as pc_decode; d_cb must be a PC_CODEBOOK_QLC codebook
  * (PC_ERR_CORRUPT in *d_status otherwise).
  */

@@ -27,8 +27,9 @@ What the pages fix, and the readings taken where they are silent:
   plot sorted PMFs): rank 0 is the most frequent symbol; equal counts are
   ranked by lower byte value first.  The in-area index is plain binary,
   most significant bit first.
-* Shannon entropy (the bound the first page compares the fixed code with)
-  is the order-0 empirical entropy of the tensor's own byte histogram.
+* Shannon entropy (the bound "Single-Stage Huffman Encoder for ML
+  Compression" compares the fixed code with) is the order-0 empirical
+  entropy of the tensor's own byte histogram.
 
 Parity pins for every function here live in ``tests/test_oracle_codebook.py``
 (brute force, closed forms, the printed Tables 1 and 2, Kraft, entropy
@@ -50,8 +51,8 @@ QLC_AREAS = 8
 QLC_PREFIX_BITS = 3
 
 # ----------------------------------------------------------------------------
-# Statistics (first page, abstract: the codebook comes from the averaged
-# distribution of earlier batches).
+# Statistics ("Single-Stage Huffman Encoder for ML Compression", abstract:
+# the codebook comes from the averaged distribution of earlier batches).
 # ----------------------------------------------------------------------------
 
 

@@ -31,9 +31,9 @@
 //      at chunk_bits); any mismatch sets *status = PC_ERR_CORRUPT.
 // A last group that is not full is a leftover: after its full groups, each
 // workgroup decodes its share of them straight from global memory.  The QLC
-// variant replaces the 12-bit table with the page's own decoder: a 3-bit
-// area number, that area's fixed-width index, and the 256-entry rank ->
-// symbol table.  Its per-area widths and first ranks sit in registers
+// variant replaces the 12-bit table with the decoder of "Quad Length Codes
+// for Lossless Compression of e4m3" (abstract): a 3-bit area number, that
+// area's fixed-width index, and the 256-entry rank -> symbol table.  Its per-area widths and first ranks sit in registers
 // (looked up with v_perm), so the decoding chain holds no memory read; only
 // the rank -> symbol read, beside the chain, goes to LDS.
 #include <atomic>
