@@ -33,7 +33,8 @@ What the pages fix, and the readings taken where they are silent:
 
 Parity pins for every function here live in ``tests/test_oracle_codebook.py``
 (brute force, closed forms, the printed Tables 1 and 2, Kraft, entropy
-bounds).  Table 1's areas 7 and 8 are not printed on the page: nothing about
+bounds).  Table 1's areas 7 and 8 are not printed in "Quad Length Codes for
+Lossless Compression of e4m3": nothing about
 them is pinned ("parity unpinned" for those two rows only).
 """
 from __future__ import annotations

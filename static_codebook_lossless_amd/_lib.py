@@ -269,7 +269,8 @@ def pc_decode(d_cb, enc: Encoded, payload_words=None, out=None, status=None):
 
 
 def pc_decode_qlc(d_cb, enc: Encoded, payload_words=None, out=None, status=None):
-    """Decode a QLC stream with the area/index decoder of the QLC page."""
+    """Decode a QLC stream with the area/index decoder of "Quad Length Codes for
+    Lossless Compression of e4m3" (abstract)."""
     return _decode(lib.pc_decode_qlc, "pc_decode_qlc", d_cb, enc, payload_words, out, status)
 
 
