@@ -152,6 +152,25 @@ def test_large_qlc_stream_both_decoders():
         del out
 
 
+@pytest.mark.parametrize("units_per_cu", [2, 3])
+def test_unit_path_few_units(units_per_cu):
+    """64 KiB chunks take the persistent unit encoder from one unit per
+    workgroup on: exactly one unit each, then one or two, with units of long
+    codes that go out in two halves and a short chunk left over; compared in
+    full with the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = units_per_cu * cus * 65536 + 1000
+    counts = random_counts(9)
+    dcb, obook = make_book(counts)
+    long_syms = np.flatnonzero(np.asarray(obook["lengths"]) >= 10).astype(np.uint8)
+    say("unit path, few units: per CU", units_per_cu, "n", n)
+    x_np = skewed(n, 300 + units_per_cu)
+    rng = np.random.default_rng(units_per_cu)
+    for u in (0, 5, units_per_cu * cus - 1):
+        x_np[u * 65536:(u + 1) * 65536] = rng.choice(long_syms, 65536)
+    roundtrip(dcb, obook, x_np, 65536)
+
+
 @pytest.mark.parametrize("chunk", [65536, 32768, 16384, 8192, 4096, 2048, 1024])
 def test_persistent_unit_path(chunk):
     """Inputs large enough for the persistent 64 KiB-unit encoder (four
