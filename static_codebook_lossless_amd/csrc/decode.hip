@@ -237,9 +237,10 @@ __device__ __forceinline__ Win4 read_win(uint32_t basem4, uint32_t q, uint32_t q
 
 // One step from the window words read a step earlier; when NEXT, it also
 // reads the next step's words.
-template <bool NEXT, class Side>
+template <bool NEXT, bool CHECK, class Side>
 __device__ __forceinline__ void lut16_step8_fast(Win4 &win, uint32_t basem4, uint32_t qlim, uint32_t &npos,
-                                                 const uint32_t *lut, uint32_t &o0, uint32_t &o1, Side &&side) {
+                                                 uint32_t &bad, const uint32_t *lut, uint32_t &o0, uint32_t &o1,
+                                                 Side &&side) {
     uint32_t h = __builtin_amdgcn_alignbit(win.w0, win.w1, npos);
     uint32_t m = __builtin_amdgcn_alignbit(win.w1, win.w2, npos);
     uint32_t l = __builtin_amdgcn_alignbit(win.w2, win.w3, npos);
@@ -252,6 +253,7 @@ __device__ __forceinline__ void lut16_step8_fast(Win4 &win, uint32_t basem4, uin
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const uint32_t ek = ecur;
+        if (CHECK) bad = bad < ek ? bad : ek;
         if (k < 7) {
             a = (h >> (ek & 31)) & kLutMask;
             ecur = *reinterpret_cast<const uint16_t *>(lb + a);
@@ -395,14 +397,17 @@ template <int MODE, bool CHECK, class Side>
 __device__ __forceinline__ uint32_t decode_half(const LdsWords &src, uint32_t pos, const Tables &t, uint32_t &bad,
                                                 uint32_t (&o)[kHalfWords], Side &&side) {
     pos = to_step_pos<MODE>(pos);
-    if (MODE == kDecodeLut12 && !CHECK) {
+    if (MODE == kDecodeLut12) {
         const uint32_t basem4 = (uint32_t)(size_t)(lds_u32 *)src.w - 4u;
         Win4 win = read_win(basem4, (31u - pos) >> 5, src.last + 1);
 #pragma unroll
         for (uint32_t q = 0; q < kHalf / 8 - 1; ++q)
-            lut16_step8_fast<true>(win, basem4, src.last + 1, pos, t.lut, o[2 * q], o[2 * q + 1], [&] { side(q); });
+            lut16_step8_fast<true, CHECK>(win, basem4, src.last + 1, pos, bad, t.lut, o[2 * q], o[2 * q + 1],
+                                          [&] { side(q); });
         constexpr uint32_t ql = kHalf / 8 - 1;
-        lut16_step8_fast<false>(win, basem4, src.last + 1, pos, t.lut, o[2 * ql], o[2 * ql + 1], [&] { side(ql); });
+        lut16_step8_fast<false, CHECK>(win, basem4, src.last + 1, pos, bad, t.lut, o[2 * ql], o[2 * ql + 1],
+                                       [&] { side(ql); });
+        if (CHECK) asm volatile("" : "+v"(bad));
     } else {
 #pragma unroll
         for (uint32_t q = 0; q < kHalf / 8; ++q) {
