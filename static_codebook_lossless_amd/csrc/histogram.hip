@@ -6,8 +6,9 @@
 // Every group of 4 lanes counts into its own 256-bin LDS copy (16 per wave):
 // same-address atomics then come from at most 4 lanes, and the copies are
 // 257 words apart so that one bin of different copies sits in different
-// banks.  Each lane keeps 4 loads of 16 bytes in flight.  A workgroup adds
-// its 64 copies into the caller's 64-bit bins at the end.
+// banks.  Each lane keeps 8 loads of 16 bytes in flight, non-temporal (the
+// bytes are read once).  A workgroup adds its 64 copies into the caller's
+// 64-bit bins at the end.
 #include "pc_internal.h"
 
 namespace pc {
@@ -17,7 +18,7 @@ constexpr uint32_t kThreads = 256;
 constexpr uint32_t kWaves = kThreads / 64;
 constexpr uint32_t kCopies = 16;  // per wave
 constexpr uint32_t kStride = 257;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 // 66 KB of LDS each: two resident workgroups per CU on 256 CUs
 constexpr uint64_t kMaxBlocks = 512;
 
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void histogram_kernel(const uint8_t *__re
     for (; i + (kUnroll - 1) * step < nq; i += kUnroll * step) {
         uint4 x[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) x[u] = q[i + u * step];
+        for (int u = 0; u < kUnroll; ++u) x[u] = load_stream16(q + i + u * step);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) count16(my, x[u]);
     }
