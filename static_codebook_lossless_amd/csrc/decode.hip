@@ -33,9 +33,10 @@
 // workgroup decodes its share of them straight from global memory.  The QLC
 // variant replaces the 12-bit table with the decoder of "Quad Length Codes
 // for Lossless Compression of e4m3" (abstract): a 3-bit area number, that
-// area's fixed-width index, and the 256-entry rank -> symbol table.  Its per-area widths and first ranks sit in registers
-// (looked up with v_perm), so the decoding chain holds no memory read; only
-// the rank -> symbol read, beside the chain, goes to LDS.
+// area's fixed-width index, and the 256-entry rank -> symbol table.  Its
+// per-area widths and first ranks sit in registers (looked up with v_perm),
+// so the decoding chain holds no memory read; only the rank -> symbol read,
+// beside the chain, goes to LDS.
 #include <atomic>
 
 #include "pc_internal.h"
@@ -954,11 +955,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const uint64_t grp = blockIdx.x;
     if (grp < num_full) {
         if (cbp->complete == 1)
-            decode_groups<MODE, false, STREAM>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo, sub_off,
-                                       n, chunk, num_sub, num_full, num_chunks, out, status);
+            decode_groups<MODE, false, STREAM>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo,
+                                               sub_off, n, chunk, num_sub, num_full, num_chunks, out, status);
         else
-            decode_groups<MODE, true, STREAM>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo, sub_off, n,
-                                      chunk, num_sub, num_full, num_chunks, out, status);
+            decode_groups<MODE, true, STREAM>(grp, tid, t, kind_ok, lds, payload, payload_words, chunk_bits, cwo,
+                                              sub_off, n, chunk, num_sub, num_full, num_chunks, out, status);
     }
     __syncthreads();  // the tables are in LDS
     decode_batch<MODE>(left, nt0, blockIdx.x, G, t, kind_ok, payload, payload_words, chunk_bits, cwo, sub_off, n,
